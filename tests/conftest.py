@@ -1,0 +1,20 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an AMD Instinct GPU (gfx950) and the built library")
+    config.addinivalue_line("markers", "slow: full-size parity case (seconds of CPU oracle time)")
+
+
+@pytest.fixture(scope="session")
+def golden_dir():
+    return GOLDEN

@@ -1,0 +1,332 @@
+"""Pins of the CPU oracle to values fixed by the source pages and by mathematics.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a value
+that does not come from the oracle itself: a hand-worked golden fixture, a closed form,
+a constructed input with a known answer, or an invariant of the definition. They are
+collected by tests/test_oracle_pins.py and re-run against planted mistakes by
+tests/test_oracle_mutations.py, which checks that each plausible mistake trips at least
+one of them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+from scipy import optimize, special, stats
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+W1E = float(special.lambertw(1.0 / math.e).real)  # W(1/e) = 0.27846...
+G_STAR = -1.0 - W1E  # argmax of |SiLU| on the negative axis
+
+
+def _closed_silu(v):
+    return v / (1.0 + math.exp(-v))
+
+
+# --------------------------------------------------------------------------- decode
+def pin_bf16_patterns():
+    fx = _load("bf16_patterns.json")
+    expect = {
+        "1": 1.0, "-3": -3.0, "1 + 2^-7": 1.0 + 2.0 ** -7, "3.140625": 3.140625,
+        "2^-133": 2.0 ** -133, "2^-126": 2.0 ** -126,
+        "(2 - 2^-7) * 2^127": (2.0 - 2.0 ** -7) * 2.0 ** 127,
+        "-0": -0.0, "inf": math.inf, "-inf": -math.inf,
+    }
+    for case in fx["cases"]:
+        got = float(oracle.bf16_to_f64(np.array([int(case["bits"], 16)], dtype=np.uint16))[0])
+        want = expect[case["value"]]
+        assert got == want, (case, got)
+        assert math.copysign(1.0, got) == math.copysign(1.0, want), case
+
+
+def pin_silu_closed_forms():
+    for k in (2.0, 3.0, 5.0, 10.0):
+        lk = math.log(k)
+        assert abs(oracle.silu(lk) - lk * k / (k + 1.0)) <= 1e-15 * lk * k
+        assert abs(oracle.silu(-lk) + lk / (k + 1.0)) <= 1e-15 * lk * k
+    assert oracle.silu(0.0) == 0.0
+    # |SiLU| peaks on the negative axis at g* = -1 - W(1/e) with value W(1/e).
+    assert abs(abs(float(oracle.silu(G_STAR))) - W1E) <= 1e-15
+    grid = np.linspace(-8.0, 0.0, 80001)
+    vals = np.abs(oracle.silu(grid))
+    assert vals.max() <= W1E + 1e-15
+    assert abs(grid[int(np.argmax(vals))] - G_STAR) <= 2e-4
+    # Large arguments: SiLU(g) -> g, SiLU(-g) -> -0.
+    assert oracle.silu(60.0) == 60.0
+    assert abs(float(oracle.silu(-800.0))) == 0.0
+
+
+def pin_relu():
+    assert list(oracle.relu([-2.0, -0.0, 0.0, 3.5])) == [0.0, 0.0, 0.0, 3.5]
+
+
+# ------------------------------------------------------------------------ FFN + mask
+def pin_reglu_golden():
+    fx = _load("reglu_tiny.json")
+    Wg, Wu, Dt = (np.array(fx[k], dtype=float) for k in ("Wg", "Wu", "Dt"))
+    b, x = np.array(fx["b"], dtype=float), np.array(fx["x"], dtype=float)
+    g, u = oracle.gate_up(Wg, Wu, x, b)
+    assert np.array_equal(g, fx["g"])
+    assert np.array_equal(oracle.dense_ffn(Wg, Wu, Dt, x, "relu", b), fx["y_dense"])
+    for case in fx["cases"]:
+        active, _, y = oracle.reglu_sequential(Wg, Wu, Dt, x, np.array(case["cand"], bool), b)
+        assert np.array_equal(active.astype(int), case["active"]), case
+        assert np.array_equal(y, case["y"]), (case, y)
+        ym = oracle.masked_ffn(Wg, Wu, Dt, x, np.array(case["cand"], bool), "relu", b)
+        assert np.array_equal(ym, case["y"]), case
+
+
+def pin_cats_golden():
+    fx = _load("cats_lnk.json")
+    l3, l2 = math.log(3.0), math.log(2.0)
+    x = np.array([l3, -l3, l2, -l2, 0.0])
+    eye = np.eye(5)
+    full = np.array([0.75 * l3 * l3, 0.25 * l3 * l3, (2.0 / 3.0) * l2 * l2, (1.0 / 3.0) * l2 * l2, 0.0])
+    a_closed = np.array([0.75 * l3, -0.25 * l3, (2.0 / 3.0) * l2, -(1.0 / 3.0) * l2, 0.0])
+    for case in fx["cases"]:
+        masks, scores, Y = oracle.cats_decode(eye, eye, eye, x[None, :], case["t"])
+        assert np.allclose(scores[0], a_closed, rtol=1e-15, atol=0), scores
+        assert np.array_equal(masks[0].astype(int), case["mask"]), (case, masks)
+        want = np.where(np.array(case["mask"], bool), full, 0.0)
+        assert np.allclose(Y[0], want, rtol=1e-14, atol=0), (case, Y)
+
+
+def pin_asymmetric_shapes():
+    """f != d with a non-symmetric Dt: y = sum_i h_i Dt[i] (rows of Dt are neurons)."""
+    Wg = np.array([[1.0, 0.0, 0.0], [0.0, 2.0, 0.0]])  # f = 2, d = 3
+    Wu = np.array([[1.0, 1.0, 1.0], [0.0, 0.0, 1.0]])
+    Dt = np.array([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0]])
+    x = np.array([1.0, 1.0, 2.0])
+    # g = [1, 2], relu = [1, 2], u = [4, 2], h = [4, 4], y = 4*[1,2,3] + 4*[4,5,6]
+    y = oracle.dense_ffn(Wg, Wu, Dt, x, "relu")
+    assert np.array_equal(y, [20.0, 28.0, 36.0]), y
+    y0 = oracle.masked_ffn(Wg, Wu, Dt, x, np.array([False, True]), "relu")
+    assert np.array_equal(y0, [16.0, 20.0, 24.0]), y0
+
+
+def _rand_layer(seed, f, d, scale=0.3):
+    g = np.random.default_rng(seed)
+    return (g.standard_normal((f, d)) * scale, g.standard_normal((f, d)) * scale,
+            g.standard_normal((f, d)) * scale, g.standard_normal(d), g.standard_normal(f) * 0.1)
+
+
+def pin_relu_zero_threshold_is_dense():
+    """ReLU with t = 0: masked FFN == dense FFN bit for bit (masked terms are exact 0)."""
+    Wg, Wu, Dt, x, b = _rand_layer(1, 24, 16)
+    m, _, Y = oracle.cats_decode(Wg, Wu, Dt, x[None], 0.0, act="relu", b=b)
+    assert np.array_equal(Y[0], oracle.dense_ffn(Wg, Wu, Dt, x, "relu", b))
+    g, _ = oracle.gate_up(Wg, Wu, x, b)
+    assert np.array_equal(m[0], g > 0)
+
+
+def pin_density_one_is_dense():
+    """t = -1 (what calibration returns for k = 0): every neuron active, masked == dense."""
+    Wg, Wu, Dt, x, _ = _rand_layer(2, 24, 16)
+    m, _, Y = oracle.cats_decode(Wg, Wu, Dt, x[None], -1.0)
+    assert m.all()
+    assert np.allclose(Y[0], oracle.dense_ffn(Wg, Wu, Dt, x), rtol=1e-13, atol=1e-13)
+
+
+def pin_mask_partition():
+    """Linearity in the mask: y(m) + y(not m) == dense; an empty mask gives y = 0."""
+    Wg, Wu, Dt, x, _ = _rand_layer(3, 40, 16)
+    m = np.random.default_rng(4).random(40) < 0.4
+    y1 = oracle.masked_ffn(Wg, Wu, Dt, x, m)
+    y2 = oracle.masked_ffn(Wg, Wu, Dt, x, ~m)
+    assert np.allclose(y1 + y2, oracle.dense_ffn(Wg, Wu, Dt, x), rtol=1e-12, atol=1e-12)
+    assert np.array_equal(oracle.masked_ffn(Wg, Wu, Dt, x, np.zeros(40, bool)), np.zeros(16))
+
+
+def pin_permutation():
+    """Permuting neurons consistently permutes the mask and leaves y unchanged."""
+    Wg, Wu, Dt, x, _ = _rand_layer(5, 32, 16)
+    perm = np.random.default_rng(6).permutation(32)
+    t = 0.2
+    m, _, Y = oracle.cats_decode(Wg, Wu, Dt, x[None], t)
+    mp, _, Yp = oracle.cats_decode(Wg[perm], Wu[perm], Dt[perm], x[None], t)
+    assert np.array_equal(mp[0], m[0][perm])
+    assert np.allclose(Yp, Y, rtol=1e-12, atol=1e-12)
+
+
+def pin_brute_force_tiny():
+    """Scalar loops, term by term, on a tiny random layer (d = 8, f = 16)."""
+    Wg, Wu, Dt, x, b = _rand_layer(7, 16, 8, scale=0.7)
+    t = 0.15
+    want_y = [0.0] * 8
+    want_m = []
+    for i in range(16):
+        gi = sum(Wg[i, j] * x[j] for j in range(8)) + b[i]
+        ui = sum(Wu[i, j] * x[j] for j in range(8))
+        ai = gi * (1.0 / (1.0 + math.exp(-gi)))
+        on = abs(ai) > t
+        want_m.append(on)
+        if on:
+            for j in range(8):
+                want_y[j] += ai * ui * Dt[i, j]
+    m, _, Y = oracle.cats_decode(Wg, Wu, Dt, x[None], t, b=b)
+    assert list(m[0]) == want_m
+    assert np.allclose(Y[0], want_y, rtol=1e-12, atol=1e-14)
+
+
+def pin_batch_union():
+    """Per-token masks in a batch: each token's result equals its single-token result;
+    the union is exactly the rows some token needs."""
+    Wg, Wu, Dt, _, _ = _rand_layer(8, 48, 16)
+    X = np.random.default_rng(9).standard_normal((4, 16))
+    t = 0.1
+    M, _, Y = oracle.cats_decode(Wg, Wu, Dt, X, t)
+    for j in range(4):
+        mj, _, yj = oracle.cats_decode(Wg, Wu, Dt, X[j][None], t)
+        assert np.array_equal(M[j], mj[0])
+        assert np.array_equal(Y[j], yj[0])
+    U = oracle.union_mask(M)
+    assert np.array_equal(U, M[0] | M[1] | M[2] | M[3])
+
+
+def pin_chunk_rows():
+    """Rows of the dense chunk are per-token dense FFNs; the chunk is not a batch mix."""
+    Wg, Wu, Dt, _, _ = _rand_layer(10, 24, 16)
+    X = np.random.default_rng(11).standard_normal((16, 16))
+    Y = oracle.dense_chunk(Wg, Wu, Dt, X)
+    for j in (0, 7, 15):
+        assert np.array_equal(Y[j], oracle.dense_ffn(Wg, Wu, Dt, X[j]))
+    # Closed form with Wu = Wg = identity: y = Dt^T (SiLU(x) * x).
+    eye = np.eye(16)
+    Yi = oracle.dense_chunk(eye, eye, Dt[:16], X)
+    want = np.array([Dt[:16].T @ (X[j] * X[j] / (1.0 + np.exp(-X[j]))) for j in range(16)])
+    assert np.allclose(Yi, want, rtol=1e-13, atol=1e-13)
+
+
+# ----------------------------------------------------------------------- calibration
+def pin_calibration_known_order():
+    fx = _load("calib_known.json")
+    Xcal = np.array([[0.3, G_STAR, 0.5], [1.0, 2.0, 3.0]])
+    named = {"SiLU(0.3)": _closed_silu(0.3), "W(1/e)": W1E, "SiLU(0.5)": _closed_silu(0.5),
+             "SiLU(2)": _closed_silu(2.0), "-1": -1.0, "inf": math.inf}
+    for case in fx["cases"]:
+        t64, t32, K, _ = oracle.calibrate_cats(np.eye(3), Xcal, case["k"])
+        assert K == case["K"], (case, K)
+        want = named[case["t"]]
+        if math.isinf(want):
+            assert math.isinf(t64) and t64 > 0
+        else:
+            assert abs(t64 - want) <= 1e-15 * max(1.0, abs(want)), (case, t64, want)
+            assert t32 == np.float32(want)
+
+
+def pin_calibration_counts():
+    """On distinct random scores exactly K are <= t and N - K pass the strict test."""
+    g = np.random.default_rng(12)
+    Wg = g.standard_normal((64, 32)) / math.sqrt(32)
+    X = g.standard_normal((20, 32))
+    for k in (0.1, 0.5, 0.7, 0.9, 0.333):
+        t, _, K, S = oracle.calibrate_cats(Wg, X, k)
+        assert K == math.floor(k * S.size + 0.5)
+        assert int((S <= t).sum()) == K
+        assert int((S > t).sum()) == S.size - K
+
+
+def _gaussian_silu_quantile(k, sigma=1.0):
+    """Closed-form k-quantile of |SiLU(sigma Z)|, Z ~ N(0,1), by root finding on
+    F(t) = P(|SiLU(sigma Z)| <= t) written with the normal CDF."""
+    f = lambda z: z / (1.0 + math.exp(-z))  # noqa: E731
+
+    def cdf(t):
+        zp = optimize.brentq(lambda z: f(z) - t, 0.0, 50.0)
+        if t >= W1E:
+            return stats.norm.cdf(zp / sigma)
+        z1 = optimize.brentq(lambda z: -f(z) - t, -60.0, G_STAR)
+        z2 = optimize.brentq(lambda z: -f(z) - t, G_STAR, 0.0)
+        return stats.norm.cdf(z1 / sigma) + stats.norm.cdf(zp / sigma) - stats.norm.cdf(z2 / sigma)
+
+    return optimize.brentq(lambda t: cdf(t) - k, 1e-9, 20.0)
+
+
+def pin_calibration_gaussian():
+    """Large iid sample: the calibrated threshold converges to the closed-form quantile."""
+    x = np.random.default_rng(13).standard_normal((2000, 500))
+    for k, tol in ((0.5, 4e-3), (0.7, 6e-3), (0.9, 1.5e-2)):
+        t, _, _, _ = oracle.calibrate_cats(np.eye(500), x, k)
+        want = _gaussian_silu_quantile(k)
+        assert abs(t - want) <= tol, (k, t, want)
+    assert abs(_gaussian_silu_quantile(0.5) - 0.254) < 2e-3
+
+
+# ------------------------------------------------------------------------------- SVD
+def _orthonormal(seed, n, k):
+    q, r = np.linalg.qr(np.random.default_rng(seed).standard_normal((n, k)))
+    return q * np.sign(np.diag(r))[None, :]
+
+
+def pin_svd_constructed():
+    """Wg = U diag(s) V^T with test-chosen s: L Q is the rank-r truncation, the
+    residual is sum_{j>r} s_j^2 (Eckart-Young), Q has orthonormal rows, and an exactly
+    rank-r matrix is reproduced."""
+    f, d, r = 40, 24, 6
+    U, V = _orthonormal(14, f, d), _orthonormal(15, d, d)
+    s = np.sort(np.random.default_rng(16).uniform(0.1, 3.0, d))[::-1]
+    Wg = (U * s) @ V.T
+    Q, L = oracle.svd_factors(Wg, r)
+    trunc = (U[:, :r] * s[:r]) @ V[:, :r].T
+    assert np.allclose(L @ Q, trunc, rtol=0, atol=1e-12)
+    res = np.linalg.norm(Wg - L @ Q) ** 2
+    assert abs(res - (s[r:] ** 2).sum()) <= 1e-10 * (s ** 2).sum()
+    assert np.allclose(Q @ Q.T, np.eye(r), atol=1e-12)
+    assert Q.shape == (r, d) and L.shape == (f, r)
+    low = (U[:, :r] * s[:r]) @ V[:, :r].T
+    Q2, L2 = oracle.svd_factors(low, r)
+    assert np.allclose(L2 @ Q2, low, atol=1e-12)
+
+
+def pin_svd_predict_full_rank():
+    """At full rank the predictor equals the biased gate, so with tau = 0 the candidate
+    set is exactly {g > 0} (Figure 3's rule) and sequential ReGLU equals dense ReGLU."""
+    Wg, Wu, Dt, x, b = _rand_layer(17, 20, 12)
+    Q, L = oracle.svd_factors(Wg, 12)
+    p = oracle.svd_predict(Q, L, x, b)
+    g, _ = oracle.gate_up(Wg, Wu, x, b)
+    assert np.allclose(p, g, atol=1e-12)
+    cand = oracle.svd_candidates(p, np.zeros(20))
+    assert np.array_equal(cand, g > 0)
+    _, _, y = oracle.reglu_sequential(Wg, Wu, Dt, x, cand, b)
+    assert np.allclose(y, oracle.dense_ffn(Wg, Wu, Dt, x, "relu", b), atol=1e-12)
+    # rank-1 closed form: Wg = a c^T  ->  p = a (c . x) + b
+    a, c = np.random.default_rng(18).standard_normal(20), np.random.default_rng(19).standard_normal(12)
+    Q1, L1 = oracle.svd_factors(np.outer(a, c), 1)
+    assert np.allclose(oracle.svd_predict(Q1, L1, x, b), a * (c @ x) + b, atol=1e-12)
+
+
+def pin_tau_golden():
+    fx = _load("tau_tiny.json")
+    P, G = np.array(fx["P"], float), np.array(fx["G"], float)
+    for case in fx["cases"]:
+        tau = oracle.calibrate_tau(P, G, case["s"])
+        assert np.allclose(tau, case["tau"], rtol=0, atol=1e-15), (case, tau)
+
+
+def pin_tau_monotone():
+    """Candidate density never rises with s (tau_i is increasing in s when m+ > m-)."""
+    g = np.random.default_rng(20)
+    G = g.standard_normal((300, 50)) - 1.0
+    P = G + 0.5 * g.standard_normal((300, 50))
+    x_p = P[:40]
+    prev = None
+    for s in (0.0, 0.2, 0.4, 0.5, 0.6, 0.8, 1.0):
+        tau = oracle.calibrate_tau(P, G, s)
+        dens = oracle.svd_candidates(x_p, tau[None, :]).mean()
+        if prev is not None:
+            assert dens <= prev + 1e-15
+        prev = dens
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
