@@ -1,0 +1,62 @@
+// Internal launch interface between the C ABI layer (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sparse_ffn.h"
+
+namespace sfn {
+
+// Control words at the start of every workspace (zero-filled once by the caller; every
+// call leaves them as it found them except the monotonically increasing release word).
+struct Ctrl {
+  uint32_t arrive;   // workgroups that finished their partial in the current launch
+  uint32_t release;  // bumped by the last arriving workgroup
+  uint32_t error;    // nonzero if a bounded wait gave up (never expected)
+  uint32_t pad[61];
+};
+static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
+
+struct DecodeArgs {
+  const char* wg;
+  const char* wu;
+  const char* wd;
+  const float* bias;  // [f] or null
+  const char* x;      // [nb, d]
+  const float* t;     // device threshold or null (0)
+  const int32_t* cand;
+  const int32_t* n_cand;
+  const uint8_t* mask_in;  // [nb, f] or null
+  float* y;                // [nb, d] or null
+  int32_t* active_idx;     // [nb, f] or null
+  int32_t* n_active;       // [nb] or null
+  Ctrl* ctrl;
+  int32_t* tile_cnt;  // [G, 4]
+  int32_t* tile_idx;  // [4, f]
+  float* part;        // [G, nb, d]
+  int d, f, nch, row_bytes, nb, act, G, n_red;
+};
+
+// Decode: workgroups for f neurons, reducing workgroups, rows a workgroup handles side
+// by side (partials per workgroup), workspace bytes, carving of the workspace.
+int decode_grid(int f);
+int decode_reducers(int G, int nb, int d);
+int decode_rows_side_by_side(int nch);
+size_t decode_workspace_bytes(int d, int f, int wb, int nb);
+void decode_carve(DecodeArgs& a, void* ws, int wb);
+hipError_t launch_decode(const DecodeArgs& a, int wdtype, hipStream_t stream);
+
+size_t chunk_workspace_bytes(int d, int f, int wdtype, int n);
+hipError_t launch_dense_chunk(const sfn_ffn& ffn, const void* x, int n, float* y, void* ws, hipStream_t stream);
+
+size_t calibrate_workspace_bytes(int d, int f, int wdtype, int n);
+hipError_t launch_calibrate(const sfn_ffn& ffn, const void* x_cal, int n, float k, float* t_out,
+                            float* scores_out, void* ws, hipStream_t stream);
+
+size_t svd_workspace_bytes(int d, int f, int r);
+hipError_t launch_svd_predict(const sfn_svd& s, const void* x, int32_t* cand, int32_t* n_cand, float* p_out,
+                              void* ws, hipStream_t stream);
+
+}  // namespace sfn

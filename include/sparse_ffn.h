@@ -1,0 +1,175 @@
+/*
+ * sparse_ffn.h -- C ABI of the contextually sparse gated-FFN decode step on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method. A gated FFN computes, for a token x in R^d,
+ *     g = Wg x (+ b),  u = Wu x,  a = act(g),  y = sum_i m_i a_i u_i Dt[i,:]
+ * where m is a 0/1 mask over the f neurons and act is SiLU (SwiGLU) or ReLU (ReGLU).
+ * Contextual sparsity picks m per token so that only the rows of Wu and Dt with m_i = 1
+ * are read:
+ *   - CATS ("CATS: Contextually-Aware Thresholding for Sparsity in Large Language
+ *     Models", abstract): m_i = [|SiLU(g_i)| > t] with one calibrated threshold t per
+ *     layer, so the dense gate itself is the score;
+ *   - SVD predictor ("SVD Contextual Sparsity Predictors for Fast LLM Inference",
+ *     abstract, Figures 1 and 3): a rank-r predictor p = L (Q x) + b with per-neuron
+ *     thresholds tau picks candidate rows; the gate is evaluated on the candidates only
+ *     and up/down only where ReLU(gate) > 0 (the sequential pipeline);
+ *   - Sirius ("SIRIUS: Contexual Sparisty with Correction for Efficient LLMs",
+ *     Approach): the full model re-runs a chunk of up to 16 tokens densely with the same
+ *     weights to verify them.
+ *
+ * Layout. Every weight matrix is row-major [f, d], one row per neuron: w_gate and w_up
+ * as in nn.Linear, and w_down_t = W_down transposed, so that the output weights of
+ * neuron i are the contiguous row i. One copy of the weights serves the sparse, dense
+ * and verification paths. Rows must be 16-byte aligned: d % 8 == 0 for bf16 and
+ * d % 4 == 0 for fp32, and every pointer 16-byte aligned.
+ *
+ * Conventions for every compute call.
+ *   - Pointers are DEVICE pointers unless marked (host). The caller owns every buffer;
+ *     the library allocates nothing and keeps no pointer after the call returns.
+ *   - The call validates its arguments on the host, enqueues its kernels on `stream`
+ *     (a hipStream_t passed as void*, NULL = the null stream) and returns without
+ *     synchronising. A negative status means nothing was enqueued, except SFN_EHIP,
+ *     which reports a launch error from the HIP runtime. Device-side faults surface at
+ *     the caller's next synchronisation. No C++ exception crosses the ABI.
+ *   - Workspace: `ws` of `ws_bytes` bytes, sized by the *_workspace_size queries. It
+ *     must be zero-filled once when it is allocated (e.g. torch.zeros); every call
+ *     leaves its control words at zero again when it completes. Calls that may run
+ *     concurrently (different streams) need distinct workspaces; calls on one stream
+ *     may share one.
+ *   - Outputs are deterministic: identical inputs give bitwise identical y, index
+ *     lists and thresholds (fixed reduction orders, no floating-point atomics).
+ *   - Arithmetic: products and sums in fp32 (bf16 inputs are widened exactly).
+ */
+#ifndef SPARSE_FFN_H
+#define SPARSE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (int). */
+#define SFN_OK 0
+#define SFN_EINVAL (-1)       /* null pointer where one is required, bad enum, k or s out of range */
+#define SFN_ESHAPE (-2)       /* d, f, r, B or n outside the supported range */
+#define SFN_EDTYPE (-3)       /* dtype not supported by this call */
+#define SFN_EWORKSPACE (-4)   /* ws NULL or ws_bytes smaller than the query returns */
+#define SFN_EALIGN (-5)       /* a pointer or a row not 16-byte aligned */
+#define SFN_EUNSUPPORTED (-6) /* valid request this build does not implement */
+#define SFN_EHIP (-7)         /* the HIP runtime reported an error on launch */
+
+/* Weight (and token) dtypes. */
+#define SFN_F32 0
+#define SFN_BF16 1
+
+/* Gate activations. */
+#define SFN_ACT_SILU 0 /* SwiGLU: a = g * sigmoid(g); CATS scores |a| */
+#define SFN_ACT_RELU 1 /* ReGLU:  a = max(g, 0) */
+
+/* Limits of this build. */
+#define SFN_MAX_BATCH 4   /* tokens per sparse_ffn_decode call */
+#define SFN_MAX_CHUNK 16  /* tokens per ffn_dense_chunk call (the Sirius chunk) */
+#define SFN_MAX_D 16384
+#define SFN_MAX_F 262144
+
+/* One FFN layer. All pointers device, each matrix [f, d] row-major in `wdtype`. */
+typedef struct sfn_ffn {
+  int32_t d;            /* hidden size */
+  int32_t f;            /* intermediate size (neurons) */
+  int32_t wdtype;       /* SFN_F32 or SFN_BF16: dtype of the three matrices and of x */
+  int32_t act;          /* SFN_ACT_SILU or SFN_ACT_RELU */
+  const void* w_gate;   /* [f, d] */
+  const void* w_up;     /* [f, d] */
+  const void* w_down_t; /* [f, d]: row i = neuron i's d output weights */
+  const float* b_gate;  /* [f] gate bias, or NULL for none */
+} sfn_ffn;
+
+/* Rank-r SVD predictor of one layer's gate (bf16 factors). All pointers device. */
+typedef struct sfn_svd {
+  int32_t d, f, r;   /* hidden size, neurons, rank (8 <= r <= 512, r % 8 == 0) */
+  int32_t reserved;  /* must be 0 */
+  const void* q;     /* [r, d] bf16: V_r^T, the top-r right singular vectors as rows */
+  const void* l;     /* [f, r] bf16: U_r diag(sigma_r) */
+  const float* b;    /* [f] gate bias added to the prediction, or NULL */
+  const float* tau;  /* [f] per-neuron thresholds: candidate iff p_i > tau_i */
+} sfn_svd;
+
+/* Host. Bytes of workspace any call on `ffn` with up to `max_tokens` tokens needs
+ * (decode: B <= 4; dense chunk: n <= 16; calibration: n tokens). 0 on invalid input.
+ * Touches no HIP state. */
+size_t sparse_ffn_workspace_size(const sfn_ffn* ffn, int32_t max_tokens);
+
+/* Host. Bytes of workspace svd_predict on `svd` needs. 0 on invalid input. */
+size_t svd_predict_workspace_size(const sfn_svd* svd);
+
+/* Host. Static, NUL-terminated description of a status code. */
+const char* sparse_ffn_strerror(int status);
+
+/*
+ * CATS threshold calibration ("CATS: Contextually-Aware Thresholding for Sparsity in
+ * Large Language Models", abstract: one threshold per layer sets the activation
+ * sparsity). Scores S = |act(x_cal Wg^T + b)| of n calibration tokens ([n, f], fp32),
+ * N = n f, K = floor(k N + 1/2); *t_out = the K-th smallest score (1-based), exact
+ * selection over the fp32 scores (radix select on their bit patterns), so that exactly
+ * K scores satisfy S <= t when they are distinct. K = 0 gives -1 (every neuron active),
+ * K = N gives +inf (none).
+ *   x_cal      [n, d] in ffn->wdtype, 1 <= n <= 65536
+ *   k          target sparsity in [0, 1]
+ *   t_out      1 float (device), written
+ *   scores_out [n, f] fp32 (device) or NULL: the scores the threshold was taken from
+ */
+int sparse_ffn_calibrate(const sfn_ffn* ffn, const void* x_cal, int32_t n, float k, float* t_out,
+                         float* scores_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One sparse decode step for B tokens (1 <= B <= 4) through one FFN layer.
+ * Scores: g = Wg x + b, a = act(g); token b's neuron i is active iff
+ *   mask_in != NULL:  mask_in[b, i] != 0                      (mask override)
+ *   otherwise:        |a_i| > *t  and (cand == NULL or i in cand)
+ * with t a device fp32 scalar (NULL means 0). Each token keeps its own mask; the rows
+ * read from Wu and Dt are the union over the batch, each read once.
+ *   y = sum_i m_bi a_bi u_bi Dt[i, :]  accumulated in fp32, [B, d] (device) or NULL to
+ *       compute the masks only (mask-only mode reads Wg alone).
+ * cand/n_cand: an ascending candidate list (from svd_predict) and its device count;
+ *   the gate is evaluated on those rows only ("SVD Contextual Sparsity Predictors for
+ *   Fast LLM Inference", Figure 3). Requires B == 1 and mask_in == NULL.
+ * active_idx [B, f] int32 / n_active [B] int32 (device) or NULL: token b's active
+ *   neurons in ascending order and their count.
+ */
+int sparse_ffn_decode(const sfn_ffn* ffn, const void* x, int32_t B, const float* t,
+                      const int32_t* cand, const int32_t* n_cand, const uint8_t* mask_in,
+                      float* y, int32_t* active_idx, int32_t* n_active, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/*
+ * SVD predictor for one token ("SVD Contextual Sparsity Predictors for Fast LLM
+ * Inference", abstract and Figures 1-3): z = Q x (fp32), p = L z + b, candidates
+ * {i : p_i > tau_i} written in ascending order.
+ *   x        [d] bf16
+ *   cand_idx [f] int32 (device), the first *n_cand entries written
+ *   n_cand   1 int32 (device)
+ *   p_out    [f] fp32 (device) or NULL: the predictions
+ */
+int svd_predict(const sfn_svd* svd, const void* x, int32_t* cand_idx, int32_t* n_cand,
+                float* p_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dense FFN over a chunk of n tokens (1 <= n <= 16), the Sirius verification pass
+ * ("SIRIUS: Contexual Sparisty with Correction for Efficient LLMs", Approach: the full
+ * model checks a chunk of sparse-generated tokens in parallel with the shared weights):
+ *   Y[j, :] = sum_i act(g_ji) u_ji Dt[i, :]   for every neuron, fp32 [n, d].
+ * bf16 weights run on matrix cores (bf16 products, fp32 accumulation; the intermediate
+ * h = act(g) u is rounded to bf16 for the second product).
+ *   x  [n, d] in ffn->wdtype;  y [n, d] fp32
+ */
+int ffn_dense_chunk(const sfn_ffn* ffn, const void* x, int32_t n, float* y, void* ws,
+                    size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_FFN_H */

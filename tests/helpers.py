@@ -1,0 +1,74 @@
+"""Shared helpers of the GPU parity tests: moving seeded inputs to the device and the
+comparison rules (mask agreement outside the threshold band, normwise output error)."""
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from contextual_activation_sparsity_amd import inputs
+
+# Output tolerances (normwise: max_j |y_j - yhat_j| / max_j |yhat_j|), fp32 accumulation
+# in both cases; bf16 weights and tokens are exact inputs, so the error is the fp32
+# summation order against float64.
+TOL_F32 = 2e-3
+TOL_BF16 = 1e-2
+# Mask mismatches are allowed only for scores within this relative distance of the
+# threshold, and at most this fraction of the neurons of a layer.
+BAND_REL = 1e-3
+MAX_MISMATCH_FRAC = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, dtype):
+    """numpy array -> contiguous device tensor. bf16 arrays arrive as uint16 patterns."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.cuda().contiguous()
+
+
+def to_f64(a, dtype):
+    return oracle.bf16_to_f64(a) if dtype == "bf16" else np.asarray(a, dtype=np.float64)
+
+
+def normwise_err(y, yhat):
+    y = np.asarray(y, dtype=np.float64)
+    yhat = np.asarray(yhat, dtype=np.float64)
+    den = np.max(np.abs(yhat))
+    return float(np.max(np.abs(y - yhat)) / den) if den > 0 else float(np.max(np.abs(y)))
+
+
+def check_mask(gpu_mask, ora_mask, score, t, abs_band=0.0, what="mask"):
+    """Masks must agree except where |score - t| <= BAND_REL |t| + abs_band; such
+    mismatches may make up at most MAX_MISMATCH_FRAC of the neurons."""
+    gpu_mask = np.asarray(gpu_mask, dtype=bool)
+    ora_mask = np.asarray(ora_mask, dtype=bool)
+    bad = gpu_mask != ora_mask
+    if not bad.any():
+        return 0
+    in_band = oracle.within_threshold_band(score, t, BAND_REL, abs_band)
+    outside = bad & ~np.broadcast_to(in_band, bad.shape)
+    assert not outside.any(), (
+        f"{what}: {int(outside.sum())} mismatches outside the band, e.g. at {np.argwhere(outside)[:5].tolist()}")
+    assert bad.sum() <= max(1, MAX_MISMATCH_FRAC * bad.size), f"{what}: {int(bad.sum())} band mismatches"
+    return int(bad.sum())
+
+
+def swiglu_layer_dev(w, layer, d=None, f=None):
+    raw = inputs.swiglu_layer(w, layer, d=d, f=f)
+    dev = {k: to_dev(v, w.dtype) for k, v in raw.items()}
+    host = {k: to_f64(v, w.dtype) for k, v in raw.items()}
+    return raw, dev, host
+
+
+def mask_from_idx(idx, n, f):
+    m = np.zeros(f, dtype=bool)
+    m[np.asarray(idx[:n], dtype=np.int64)] = True
+    return m

@@ -1,0 +1,138 @@
+"""C-ABI conventions on the CPU: the library loads, exports every function the header
+declares, and rejects invalid arguments with the documented status before any HIP call
+(so these run without a GPU and never launch a kernel)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_ffn.h")
+
+try:
+    from contextual_activation_sparsity_amd import binding as B
+except ImportError as e:  # library not built
+    B = None
+    _why = str(e)
+
+needs_lib = pytest.mark.skipif(B is None, reason="libsparse_ffn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ("sparse_ffn_calibrate", "sparse_ffn_decode", "svd_predict", "ffn_dense_chunk",
+              "sparse_ffn_workspace_size", "svd_predict_workspace_size", "sparse_ffn_strerror"):
+        assert n in names, (n, names)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = B.raw()
+    for n in declared_functions():
+        assert hasattr(lib, n), f"libsparse_ffn.so does not export {n}"
+    assert set(B.EXPORTED) == set(declared_functions())
+
+
+@needs_lib
+def test_strerror_covers_codes():
+    for code in range(0, -8, -1):
+        s = B.sparse_ffn_strerror(code)
+        assert s and s != "unknown status"
+    assert B.sparse_ffn_strerror(-99) == "unknown status"
+
+
+FAKE = 0x100000  # 256-aligned fake device address; never dereferenced on these paths
+
+
+def _ffn(d=4096, f=11008, wdtype=None, act=0, wg=FAKE, wu=FAKE, wd=FAKE, b=None):
+    wdtype = B.SFN_BF16 if wdtype is None else wdtype
+    return B.sfn_ffn(d, f, wdtype, act, wg, wu, wd, b)
+
+
+@needs_lib
+def test_workspace_size_queries():
+    lib = B.raw()
+    ffn = _ffn()
+    n1 = lib.sparse_ffn_workspace_size(ctypes.byref(ffn), 1)
+    n4 = lib.sparse_ffn_workspace_size(ctypes.byref(ffn), 4)
+    n256 = lib.sparse_ffn_workspace_size(ctypes.byref(ffn), 256)
+    assert 0 < n1 <= n4 <= n256
+    assert n256 >= 256 * 11008 * 4  # calibration scores
+    assert lib.sparse_ffn_workspace_size(ctypes.byref(ffn), 0) == 0
+    assert lib.sparse_ffn_workspace_size(None, 1) == 0
+    assert lib.sparse_ffn_workspace_size(ctypes.byref(_ffn(d=4100)), 1) == 0  # bf16 row not 16-B
+    assert lib.sparse_ffn_workspace_size(ctypes.byref(_ffn(wdtype=7)), 1) == 0
+    svd = B.sfn_svd(4096, 11008, 256, 0, FAKE, FAKE, None, FAKE)
+    assert lib.svd_predict_workspace_size(ctypes.byref(svd)) > 0
+    assert lib.svd_predict_workspace_size(ctypes.byref(B.sfn_svd(4096, 11008, 1024, 0, FAKE, FAKE, None, FAKE))) == 0
+
+
+@needs_lib
+def test_decode_validation():
+    lib = B.raw()
+    ffn = _ffn()
+    ws_need = lib.sparse_ffn_workspace_size(ctypes.byref(ffn), 1)
+    call = lambda **kw: lib.sparse_ffn_decode(  # noqa: E731
+        kw.get("ffn", ctypes.byref(ffn)), kw.get("x", FAKE), kw.get("B", 1), kw.get("t", FAKE),
+        kw.get("cand", None), kw.get("n_cand", None), kw.get("mask", None), kw.get("y", FAKE),
+        kw.get("idx", None), kw.get("n_act", None), kw.get("ws", FAKE), kw.get("ws_bytes", ws_need), None)
+    assert call(ffn=None) == B.SFN_EINVAL
+    assert call(x=None) == B.SFN_EINVAL
+    assert call(x=FAKE + 4) == B.SFN_EALIGN
+    assert call(B=0) == B.SFN_ESHAPE
+    assert call(B=5) == B.SFN_ESHAPE
+    assert call(cand=FAKE) == B.SFN_EINVAL  # cand without n_cand
+    assert call(cand=FAKE, n_cand=FAKE, B=2) == B.SFN_EINVAL
+    assert call(cand=FAKE, n_cand=FAKE, mask=FAKE) == B.SFN_EINVAL
+    assert call(ws=None) == B.SFN_EWORKSPACE
+    assert call(ws_bytes=ws_need - 1) == B.SFN_EWORKSPACE
+    assert call(ws=FAKE + 16) == B.SFN_EALIGN
+    assert call(y=FAKE + 8) == B.SFN_EALIGN
+    assert call(ffn=ctypes.byref(_ffn(wdtype=3))) == B.SFN_EDTYPE
+    assert call(ffn=ctypes.byref(_ffn(act=5))) == B.SFN_EINVAL
+    assert call(ffn=ctypes.byref(_ffn(f=0))) == B.SFN_ESHAPE
+    assert call(ffn=ctypes.byref(_ffn(d=0))) == B.SFN_ESHAPE
+    assert call(ffn=ctypes.byref(_ffn(wu=None))) == B.SFN_EINVAL  # y requested needs up/down
+    assert call(ffn=ctypes.byref(_ffn(wg=FAKE + 2))) == B.SFN_EALIGN
+    # batch 4 needs the larger workspace
+    assert call(B=4, x=FAKE) == B.SFN_EWORKSPACE
+
+
+@needs_lib
+def test_other_calls_validation():
+    lib = B.raw()
+    ffn = _ffn()
+    need = lib.sparse_ffn_workspace_size(ctypes.byref(ffn), 256)
+    cal = lambda **kw: lib.sparse_ffn_calibrate(  # noqa: E731
+        ctypes.byref(ffn), kw.get("x", FAKE), kw.get("n", 256), kw.get("k", 0.5), kw.get("t", FAKE),
+        None, kw.get("ws", FAKE), kw.get("ws_bytes", need), None)
+    assert cal(k=1.5) == B.SFN_EINVAL
+    assert cal(k=-0.1) == B.SFN_EINVAL
+    assert cal(k=float("nan")) == B.SFN_EINVAL
+    assert cal(n=0) == B.SFN_ESHAPE
+    assert cal(t=None) == B.SFN_EINVAL
+    assert cal(ws_bytes=100) == B.SFN_EWORKSPACE
+    chunk = lambda **kw: lib.ffn_dense_chunk(  # noqa: E731
+        ctypes.byref(ffn), kw.get("x", FAKE), kw.get("n", 16), kw.get("y", FAKE), FAKE, need, None)
+    assert chunk(n=17) == B.SFN_ESHAPE
+    assert chunk(n=0) == B.SFN_ESHAPE
+    assert chunk(y=None) == B.SFN_EINVAL
+    svd = B.sfn_svd(4096, 11008, 256, 0, FAKE, FAKE, None, FAKE)
+    sneed = lib.svd_predict_workspace_size(ctypes.byref(svd))
+    pred = lambda s=svd, **kw: lib.svd_predict(  # noqa: E731
+        ctypes.byref(s), kw.get("x", FAKE), kw.get("cand", FAKE), kw.get("n", FAKE), None, FAKE,
+        kw.get("ws_bytes", sneed), None)
+    assert pred(cand=None) == B.SFN_EINVAL
+    assert pred(ws_bytes=sneed - 1) == B.SFN_EWORKSPACE
+    assert pred(s=B.sfn_svd(4096, 11008, 252, 0, FAKE, FAKE, None, FAKE)) == B.SFN_EALIGN
+    assert pred(s=B.sfn_svd(4096, 11008, 256, 1, FAKE, FAKE, None, FAKE)) == B.SFN_EINVAL
+    assert pred(s=B.sfn_svd(4096, 11008, 256, 0, FAKE, FAKE, None, None)) == B.SFN_EINVAL

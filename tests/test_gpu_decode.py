@@ -1,0 +1,214 @@
+"""GPU parity of sparse_ffn_decode against the CPU oracle (dense FFN, then mask).
+
+Each case draws seeded synthetic inputs, runs the library through the C ABI and checks:
+  * active sets: equal to the oracle's except for scores within 1e-3 relative of the
+    threshold, at most 0.1% of the neurons;
+  * outputs on the oracle's own mask (passed in as the mask override): normwise error
+    <= 2e-3 (fp32 weights) / 1e-2 (bf16 weights), fp32 accumulation;
+  * outputs on the library's own mask against the oracle on that same mask.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from contextual_activation_sparsity_amd import inputs
+from tests.helpers import (TOL_BF16, TOL_F32, check_mask, mask_from_idx, normwise_err, say,
+                           swiglu_layer_dev, to_dev, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from contextual_activation_sparsity_amd import binding as B
+
+
+def _tol(dtype):
+    return TOL_BF16 if dtype == "bf16" else TOL_F32
+
+
+def _ctrl_error(ws):
+    return int(ws[8:12].view(torch.int32).item())
+
+
+def run_decode(layer, x_dev, t_val, ws, mask=None, want_y=True, cand=None, n_cand=None):
+    Bn = x_dev.shape[0]
+    t = torch.tensor([t_val], dtype=torch.float32, device="cuda") if t_val is not None else None
+    y = torch.full((Bn, layer.d), float("nan"), dtype=torch.float32, device="cuda") if want_y else None
+    idx = torch.full((Bn, layer.f), -1, dtype=torch.int32, device="cuda")
+    n_act = torch.full((Bn,), -1, dtype=torch.int32, device="cuda")
+    m = torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).cuda() if mask is not None else None
+    B.sparse_ffn_decode(layer, x_dev, t, ws, y=y, mask_in=m, active_idx=idx, n_active=n_act, cand=cand,
+                        n_cand=n_cand)
+    torch.cuda.synchronize()
+    assert _ctrl_error(ws) == 0
+    return (y.cpu().numpy() if want_y else None), idx.cpu().numpy(), n_act.cpu().numpy()
+
+
+def _case(w, d, f, k, n_tok, seed_layer=0, batch=1, act="silu"):
+    """Calibrate t with the oracle on the workload's calibration tokens, run n_tok
+    decode tokens in batches, compare with the oracle."""
+    say(f"[decode] workload={w.name} d={d} f={f} k={k} tokens={n_tok} batch={batch}")
+    raw, dev, host = swiglu_layer_dev(w, seed_layer, d=d, f=f)
+    Wg, Wu, Dt = host["w_gate"], host["w_up"], host["w_down_t"]
+    xcal = to_f64(inputs.tokens(w, w.n_cal, inputs.STREAM_CAL, d=d), w.dtype)
+    _, t32, K, _ = oracle.calibrate_cats(Wg, xcal, k)
+    t = float(t32)
+    xs_raw = inputs.tokens(w, n_tok, inputs.STREAM_DECODE, d=d)
+    xs = to_f64(xs_raw, w.dtype)
+    layer = B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"],
+                       act=B.SFN_ACT_SILU if act == "silu" else B.SFN_ACT_RELU)
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, batch))
+    tol = _tol(w.dtype)
+    worst = 0.0
+    mism = 0
+    for j0 in range(0, n_tok, batch):
+        xb = xs[j0:j0 + batch]
+        xd = to_dev(xs_raw[j0:j0 + batch], w.dtype)
+        om, oa, _ = oracle.cats_decode(Wg, Wu, Dt, xb, t, act=act)
+        y, idx, n_act = run_decode(layer, xd, t, ws)
+        for b in range(xb.shape[0]):
+            gm = mask_from_idx(idx[b], n_act[b], f)
+            assert np.all(np.diff(idx[b][:n_act[b]]) > 0), "active indices ascending"
+            mism += check_mask(gm, om[b], np.abs(oa[b]), t, what=f"token {j0 + b}")
+            # own mask: compare with the oracle on the library's mask
+            y_own = oracle.masked_ffn(Wg, Wu, Dt, xb[b], gm, act)
+            e1 = normwise_err(y[b], y_own)
+            assert e1 <= tol, (j0 + b, e1)
+            worst = max(worst, e1)
+        # oracle's mask through the override
+        y2, idx2, n2 = run_decode(layer, xd, t, ws, mask=om.astype(np.uint8))
+        for b in range(xb.shape[0]):
+            yo = oracle.masked_ffn(Wg, Wu, Dt, xb[b], om[b], act)
+            e2 = normwise_err(y2[b], yo)
+            assert e2 <= tol, (j0 + b, e2)
+            assert n2[b] == om[b].sum()
+            assert np.array_equal(np.sort(idx2[b][:n2[b]]), np.flatnonzero(om[b]))
+    say(f"    worst normwise err {worst:.3e}, band mismatches {mism}")
+    return layer, ws, dev, host, t
+
+
+def test_tiny_fp32_all_tokens():
+    w = inputs.workload(0)
+    _case(w, w.d, w.f, 0.5, w.decode_tokens)
+
+
+@pytest.mark.parametrize("d,f", [(512, 1000), (1024, 777), (128, 300), (8192, 2000), (2048, 4099)])
+def test_ragged_shapes_bf16(d, f):
+    w = inputs.workload(1)
+    _case(w, d, f, 0.5, 4)
+
+
+@pytest.mark.parametrize("d,f", [(96, 500), (1024, 1030), (2048, 3000)])
+def test_ragged_shapes_f32(d, f):
+    w = inputs.workload(0)
+    _case(w, d, f, 0.6, 4)
+
+
+@pytest.mark.parametrize("k", [0.5, 0.7])
+def test_llama2_7b_layer(k):
+    w = inputs.workload(1)
+    _case(w, w.d, w.f, k, 4)
+
+
+def test_batch4_union_llama3_8b_layer():
+    w = inputs.workload(2)
+    layer, ws, dev, host, t = _case(w, w.d, w.f, 0.5, 8, batch=4)
+    # each token of the batch equals its single-token run (same mask, same output up to
+    # the fixed reduction order of the split-k partials)
+    xs_raw = inputs.tokens(w, 4, inputs.STREAM_DECODE)
+    y4, idx4, n4 = run_decode(layer, to_dev(xs_raw, w.dtype), t, ws)
+    ws1 = B.workspace(B.sparse_ffn_workspace_size(layer, 1))
+    for b in range(4):
+        y1, idx1, n1 = run_decode(layer, to_dev(xs_raw[b:b + 1], w.dtype), t, ws1)
+        assert n1[0] == n4[b]
+        assert np.array_equal(idx1[0][:n1[0]], idx4[b][:n4[b]])
+        assert normwise_err(y4[b], y1[0]) <= 1e-5
+
+
+@pytest.mark.parametrize("batch", [2, 3])
+def test_partial_batches(batch):
+    w = inputs.workload(1)
+    _case(w, 1024, 2500, 0.5, 6, batch=batch)
+
+
+def test_density_one_is_dense_and_relu_zero_is_dense():
+    w = inputs.workload(1)
+    d, f = 1024, 3000
+    raw, dev, host = swiglu_layer_dev(w, 3, d=d, f=f)
+    Wg, Wu, Dt = host["w_gate"], host["w_up"], host["w_down_t"]
+    xs_raw = inputs.tokens(w, 2, inputs.STREAM_DECODE, d=d)
+    xs = to_f64(xs_raw, w.dtype)
+    for act, t in (("silu", -1.0), ("relu", 0.0)):
+        say(f"[decode] dense equivalence act={act} t={t}")
+        layer = B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"],
+                           act=B.SFN_ACT_SILU if act == "silu" else B.SFN_ACT_RELU)
+        ws = B.workspace(B.sparse_ffn_workspace_size(layer, 2))
+        y, idx, n_act = run_decode(layer, to_dev(xs_raw, w.dtype), t, ws)
+        for b in range(2):
+            yd = oracle.dense_ffn(Wg, Wu, Dt, xs[b], act)
+            assert normwise_err(y[b], yd) <= TOL_BF16
+            if act == "silu":
+                assert n_act[b] == f
+            else:
+                g, _ = oracle.gate_up(Wg, Wu, xs[b])
+                sig = np.sqrt((Wg * Wg).sum(1)) * np.sqrt((xs[b] ** 2).mean())
+                check_mask(mask_from_idx(idx[b], n_act[b], f), g > 0, g, 0.0, abs_band=1e-3 * sig)
+
+
+def test_mask_only_and_empty_mask_and_determinism():
+    w = inputs.workload(1)
+    d, f = 4096, 11008
+    raw, dev, host = swiglu_layer_dev(w, 0, d=d, f=f)
+    layer = B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"])
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, 1))
+    x_raw = inputs.tokens(w, 1, inputs.STREAM_DECODE)
+    xd = to_dev(x_raw, w.dtype)
+    say("[decode] mask-only mode")
+    _, idx_m, n_m = run_decode(layer, xd, 0.265, ws, want_y=False)
+    y_a, idx_a, n_a = run_decode(layer, xd, 0.265, ws)
+    assert n_m[0] == n_a[0] and np.array_equal(idx_m[0][:n_m[0]], idx_a[0][:n_a[0]])
+    say("[decode] determinism")
+    for _ in range(3):
+        y_b, idx_b, n_b = run_decode(layer, xd, 0.265, ws)
+        assert np.array_equal(y_a.view(np.uint32), y_b.view(np.uint32))
+        assert np.array_equal(idx_a, idx_b) and np.array_equal(n_a, n_b)
+    say("[decode] empty mask")
+    y0, _, n0 = run_decode(layer, xd, 0.265, ws, mask=np.zeros((1, f), np.uint8))
+    assert n0[0] == 0 and np.all(y0 == 0.0)
+    say("[decode] threshold above every score")
+    y1, _, n1 = run_decode(layer, xd, 1e30, ws)
+    assert n1[0] == 0 and np.all(y1 == 0.0)
+
+
+def test_candidate_mode_reglu():
+    """Gate evaluated on a candidate list only (ReLU, bias): oracle reglu_sequential."""
+    w = inputs.workload(3)
+    d, f = 2048, 5000
+    raw = inputs.reglu_layer(w, 0, d=d, f=f)
+    Wg, Wu, Dt = (to_f64(raw[k], "bf16") for k in ("w_gate", "w_up", "w_down_t"))
+    b = raw["b_gate"].astype(np.float64)
+    layer = B.FFNLayer(to_dev(raw["w_gate"], "bf16"), to_dev(raw["w_up"], "bf16"), to_dev(raw["w_down_t"], "bf16"),
+                       b_gate=torch.from_numpy(raw["b_gate"]).cuda(), act=B.SFN_ACT_RELU)
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, 1))
+    xs_raw = inputs.tokens(w, 3, inputs.STREAM_DECODE, d=d)
+    xs = to_f64(xs_raw, "bf16")
+    rng = np.random.default_rng(5)
+    for j, dens in enumerate((0.25, 0.0, 1.0)):
+        say(f"[decode] candidate mode density {dens}")
+        cand = np.flatnonzero(rng.random(f) < dens).astype(np.int32)
+        cm = np.zeros(f, bool)
+        cm[cand] = True
+        cand_d = torch.from_numpy(np.concatenate([cand, np.zeros(f - len(cand), np.int32)])).cuda()
+        n_cand = torch.tensor([len(cand)], dtype=torch.int32, device="cuda")
+        y, idx, n_act = run_decode(layer, to_dev(xs_raw[j:j + 1], "bf16"), 0.0, ws, cand=cand_d, n_cand=n_cand)
+        active, g, yo = oracle.reglu_sequential(Wg, Wu, Dt, xs[j], cm, b)
+        sig = np.sqrt((Wg * Wg).sum(1)) * np.sqrt((xs[j] ** 2).mean())
+        gm = mask_from_idx(idx[0], n_act[0], f)
+        check_mask(gm, active, g, 0.0, abs_band=1e-3 * sig)
+        assert not (gm & ~cm).any(), "active outside the candidate set"
+        _, _, y_own = oracle.reglu_sequential(Wg, Wu, Dt, xs[j], gm, b)
+        if np.abs(y_own).max() > 0:
+            assert normwise_err(y[0], y_own) <= TOL_BF16
+        else:
+            assert np.all(y[0] == 0.0)

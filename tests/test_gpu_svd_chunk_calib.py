@@ -1,0 +1,172 @@
+"""GPU parity of svd_predict, ffn_dense_chunk and sparse_ffn_calibrate against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from contextual_activation_sparsity_amd import inputs
+from tests.helpers import (TOL_BF16, TOL_F32, check_mask, mask_from_idx, normwise_err, say,
+                           swiglu_layer_dev, to_dev, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from contextual_activation_sparsity_amd import binding as B
+
+
+# ------------------------------------------------------------------------------ SVD
+def _svd_case(d, f, r, s, n_tok, n_cal=256, rank_struct=256):
+    w = inputs.workload(3)
+    say(f"[svd] d={d} f={f} r={r} s={s}")
+    raw = inputs.reglu_layer(w, 0, d=d, f=f, rank_struct=rank_struct)
+    Wg = to_f64(raw["w_gate"], "bf16")
+    b = raw["b_gate"].astype(np.float64)
+    Q, L = oracle.svd_factors(Wg, r)
+    Qb, Lb = inputs.f32_to_bf16_bits(Q), inputs.f32_to_bf16_bits(L)
+    Q64, L64 = to_f64(Qb, "bf16"), to_f64(Lb, "bf16")
+    xcal = to_f64(inputs.tokens(w, n_cal, inputs.STREAM_TAU, d=d), "bf16")
+    P = np.array([oracle.svd_predict(Q64, L64, xc, b) for xc in xcal])
+    G = xcal @ Wg.T + b
+    tau = oracle.calibrate_tau(P, G, s).astype(np.float32)
+    pred = B.SVDPredictor(to_dev(Qb, "bf16"), to_dev(Lb, "bf16"), torch.from_numpy(tau).cuda(),
+                          b=torch.from_numpy(raw["b_gate"]).cuda())
+    ws = B.workspace(B.svd_predict_workspace_size(pred))
+    xs_raw = inputs.tokens(w, n_tok, inputs.STREAM_DECODE, d=d)
+    xs = to_f64(xs_raw, "bf16")
+    dens = []
+    for j in range(n_tok):
+        cand = torch.full((f,), -1, dtype=torch.int32, device="cuda")
+        n_cand = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        p_out = torch.empty(f, dtype=torch.float32, device="cuda")
+        B.svd_predict(pred, to_dev(xs_raw[j], "bf16"), cand, n_cand, ws, p_out=p_out)
+        torch.cuda.synchronize()
+        p_ref = oracle.svd_predict(Q64, L64, xs[j], b)
+        p_gpu = p_out.cpu().numpy()
+        scale = np.sqrt((L64 ** 2).sum(1)) * np.linalg.norm(Q64 @ xs[j]) / np.sqrt(r) + 1e-30
+        assert np.max(np.abs(p_gpu - p_ref) / (np.abs(p_ref) + scale)) < 1e-4
+        nc = int(n_cand.item())
+        ci = cand.cpu().numpy()
+        assert np.all(np.diff(ci[:nc]) > 0), "candidates ascending"
+        cm_ref = oracle.svd_candidates(p_ref, tau)
+        check_mask(mask_from_idx(ci, nc, f), cm_ref, p_ref, tau.astype(np.float64), abs_band=1e-3 * scale,
+                   what=f"candidates token {j}")
+        dens.append(nc / f)
+    return raw, pred, ws, (Q64, L64, b, tau), np.array(dens)
+
+
+@pytest.mark.parametrize("d,f,r", [(512, 1000, 64), (1024, 3000, 128), (2048, 700, 352), (4096, 11008, 256)])
+def test_svd_predict(d, f, r):
+    _svd_case(d, f, r, 0.5, 3)
+
+
+def test_svd_sequential_pipeline_end_to_end():
+    """svd_predict -> sparse_ffn_decode(cand, ReLU, t=0) against oracle.reglu_sequential."""
+    d, f, r = 4096, 11008, 256
+    raw, pred, ws_p, (Q64, L64, b, tau), dens = _svd_case(d, f, r, 0.5, 2)
+    Wg, Wu, Dt = (to_f64(raw[k], "bf16") for k in ("w_gate", "w_up", "w_down_t"))
+    layer = B.FFNLayer(to_dev(raw["w_gate"], "bf16"), to_dev(raw["w_up"], "bf16"), to_dev(raw["w_down_t"], "bf16"),
+                       b_gate=torch.from_numpy(raw["b_gate"]).cuda(), act=B.SFN_ACT_RELU)
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, 1))
+    w = inputs.workload(3)
+    xs_raw = inputs.tokens(w, 2, inputs.STREAM_DECODE, d=d)
+    xs = to_f64(xs_raw, "bf16")
+    for j in range(2):
+        say(f"[svd+decode] token {j}")
+        xd = to_dev(xs_raw[j:j + 1], "bf16")
+        cand = torch.empty(f, dtype=torch.int32, device="cuda")
+        n_cand = torch.empty(1, dtype=torch.int32, device="cuda")
+        B.svd_predict(pred, xd, cand, n_cand, ws_p)
+        y = torch.empty((1, d), dtype=torch.float32, device="cuda")
+        idx = torch.empty((1, f), dtype=torch.int32, device="cuda")
+        n_act = torch.empty(1, dtype=torch.int32, device="cuda")
+        B.sparse_ffn_decode(layer, xd, None, ws, y=y, cand=cand, n_cand=n_cand, active_idx=idx, n_active=n_act)
+        torch.cuda.synchronize()
+        cm = mask_from_idx(cand.cpu().numpy(), int(n_cand.item()), f)
+        act_gpu = mask_from_idx(idx.cpu().numpy()[0], int(n_act.item()), f)
+        active, g, _ = oracle.reglu_sequential(Wg, Wu, Dt, xs[j], cm, b)
+        sig = np.sqrt((Wg * Wg).sum(1)) * np.sqrt((xs[j] ** 2).mean())
+        check_mask(act_gpu, active, g, 0.0, abs_band=1e-3 * sig)
+        _, _, y_own = oracle.reglu_sequential(Wg, Wu, Dt, xs[j], act_gpu, b)
+        assert normwise_err(y.cpu().numpy()[0], y_own) <= TOL_BF16
+        say(f"    candidates {cm.mean():.3f} active {act_gpu.mean():.3f}")
+
+
+# ---------------------------------------------------------------------------- chunk
+@pytest.mark.parametrize("d,f,n", [(4096, 11008, 16), (1024, 3000, 5), (512, 1001, 1), (8192, 2048, 16),
+                                   (2048, 4100, 9)])
+def test_dense_chunk_bf16(d, f, n):
+    w = inputs.workload(4)
+    say(f"[chunk] d={d} f={f} n={n}")
+    raw, dev, host = swiglu_layer_dev(w, 0, d=d, f=f)
+    layer = B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"])
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, 16))
+    xs_raw = inputs.tokens(w, n, inputs.STREAM_DECODE, d=d)
+    xs = to_f64(xs_raw, "bf16")
+    y = torch.full((n, d), float("nan"), dtype=torch.float32, device="cuda")
+    B.ffn_dense_chunk(layer, to_dev(xs_raw, "bf16"), y, ws)
+    torch.cuda.synchronize()
+    Y = y.cpu().numpy()
+    Yo = oracle.dense_chunk(host["w_gate"], host["w_up"], host["w_down_t"], xs)
+    for j in range(n):
+        assert normwise_err(Y[j], Yo[j]) <= TOL_BF16, j
+    # a row of the chunk does not depend on the other rows
+    y1 = torch.empty((1, d), dtype=torch.float32, device="cuda")
+    B.ffn_dense_chunk(layer, to_dev(xs_raw[n - 1:n], "bf16"), y1, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(y1.cpu().numpy()[0].view(np.uint32), Y[n - 1].view(np.uint32))
+
+
+def test_dense_chunk_f32_and_bias_relu():
+    w = inputs.workload(0)
+    d, f, n = 256, 688, 7
+    say("[chunk] fp32")
+    raw, dev, host = swiglu_layer_dev(w, 0, d=d, f=f)
+    bias = np.random.default_rng(3).standard_normal(f).astype(np.float32) * 0.1
+    for act in ("silu", "relu"):
+        layer = B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"], b_gate=torch.from_numpy(bias).cuda(),
+                           act=B.SFN_ACT_SILU if act == "silu" else B.SFN_ACT_RELU)
+        ws = B.workspace(B.sparse_ffn_workspace_size(layer, 16))
+        xs_raw = inputs.tokens(w, n, inputs.STREAM_DECODE, d=d)
+        y = torch.empty((n, d), dtype=torch.float32, device="cuda")
+        B.ffn_dense_chunk(layer, to_dev(xs_raw, "f32"), y, ws)
+        torch.cuda.synchronize()
+        Yo = oracle.dense_chunk(host["w_gate"], host["w_up"], host["w_down_t"], to_f64(xs_raw, "f32"), act,
+                                bias.astype(np.float64))
+        for j in range(n):
+            assert normwise_err(y.cpu().numpy()[j], Yo[j]) <= TOL_F32
+
+
+# ---------------------------------------------------------------------- calibration
+@pytest.mark.parametrize("wi,d,f,n,k", [(0, 256, 688, 256, 0.5), (1, 4096, 11008, 256, 0.5),
+                                         (1, 4096, 11008, 256, 0.7), (1, 1024, 999, 33, 0.3),
+                                         (1, 512, 700, 20, 0.0), (1, 512, 700, 20, 1.0)])
+def test_calibrate(wi, d, f, n, k):
+    w = inputs.workload(wi)
+    say(f"[calibrate] workload={wi} d={d} f={f} n={n} k={k}")
+    raw, dev, host = swiglu_layer_dev(w, 0, d=d, f=f)
+    layer = B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"])
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, n))
+    xcal_raw = inputs.tokens(w, n, inputs.STREAM_CAL, d=d)
+    t_out = torch.empty(1, dtype=torch.float32, device="cuda")
+    S = torch.empty((n, f), dtype=torch.float32, device="cuda")
+    B.sparse_ffn_calibrate(layer, to_dev(xcal_raw, w.dtype), k, t_out, ws, scores_out=S)
+    torch.cuda.synchronize()
+    t_gpu = float(t_out.item())
+    k32 = float(np.float32(k))
+    t64, t32, K, S_ref = oracle.calibrate_cats(host["w_gate"], to_f64(xcal_raw, w.dtype), k32)
+    if K == 0:
+        assert t_gpu == -1.0
+        return
+    if K == S_ref.size:
+        assert np.isinf(t_gpu) and t_gpu > 0
+        return
+    Sg = S.cpu().numpy().astype(np.float64)
+    # exact selection on the library's own scores
+    assert int((Sg < t_gpu).sum()) < K <= int((Sg <= t_gpu).sum())
+    assert t_gpu in set(Sg.ravel().tolist())
+    # scores agree with the oracle to fp32 accumulation accuracy ...
+    err = np.max(np.abs(Sg - S_ref))
+    assert err <= 1e-5 * max(1.0, np.max(S_ref))
+    # ... and order statistics are 1-Lipschitz in the max norm
+    assert abs(t_gpu - t64) <= err + 1e-7
