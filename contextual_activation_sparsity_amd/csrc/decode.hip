@@ -150,7 +150,7 @@ struct DecodeKernel {
       const int n = min(max(*a.n_cand, 0), a.f);  // a count beyond f cannot be a valid list
       r0 = (int)((long long)w * n / a.G);
       nrows = (int)((long long)(w + 1) * n / a.G) - r0;
-      for (int i = tid; i < nrows; i += kNT) sm.rowid[i] = a.cand[r0 + i];
+      for (int i = tid; i < nrows; i += kNT) sm.rowid[i] = min(max(a.cand[r0 + i], 0), a.f - 1);  // stay in bounds
     } else {
       r0 = (int)((long long)w * a.f / a.G);
       nrows = (int)((long long)(w + 1) * a.f / a.G) - r0;
