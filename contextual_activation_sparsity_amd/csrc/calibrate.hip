@@ -136,7 +136,7 @@ __global__ void set_kernel(float* t_out, float v) { *t_out = v; }
 size_t calibrate_workspace_bytes(int d, int f, int wdtype, int n) {
   (void)d;
   (void)wdtype;
-  return sizeof(SelState) + (((size_t)n * f * sizeof(float) + 255) & ~(size_t)255);
+  return kWsHeader + sizeof(SelState) + (((size_t)n * f * sizeof(float) + 255) & ~(size_t)255);
 }
 
 hipError_t launch_calibrate(const sfn_ffn& ffn, const void* x_cal, int n, float k, float* t_out, float* scores_out,
@@ -152,8 +152,9 @@ hipError_t launch_calibrate(const sfn_ffn& ffn, const void* x_cal, int n, float 
     hipLaunchKernelGGL(set_kernel, dim3(1), dim3(1), 0, stream, t_out, __builtin_huge_valf());
     return hipGetLastError();
   }
-  SelState* st = static_cast<SelState*>(ws);
-  float* S = scores_out ? scores_out : reinterpret_cast<float*>(static_cast<char*>(ws) + sizeof(SelState));
+  SelState* st = reinterpret_cast<SelState*>(static_cast<char*>(ws) + kWsHeader);
+  float* S = scores_out ? scores_out
+                        : reinterpret_cast<float*>(static_cast<char*>(ws) + kWsHeader + sizeof(SelState));
   const dim3 sgrid((ffn.f + kNeurTile - 1) / kNeurTile, (n + kTokTile - 1) / kTokTile);
   if (ffn.wdtype == SFN_BF16) {
     hipLaunchKernelGGL(score_kernel<WT_BF16>, sgrid, dim3(256), 0, stream, static_cast<const char*>(ffn.w_gate),

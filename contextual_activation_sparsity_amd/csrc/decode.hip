@@ -327,6 +327,12 @@ struct DecodeKernel {
     __syncthreads();
     const uint32_t ticket = sm.ticket;
     const uint32_t first_red = (uint32_t)(a.G - a.n_red);
+    if (ticket >= (uint32_t)a.G) {
+      // control words not zero at launch (workspace not zero-filled, or shared by
+      // overlapping calls): flag it and write nothing rather than out of range
+      if (tid == 0) __hip_atomic_store(&a.ctrl->error, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
     if (ticket < first_red) return;
     if (tid == 0) {
       if (ticket == (uint32_t)(a.G - 1)) {
@@ -454,7 +460,7 @@ size_t decode_workspace_bytes(int d, int f, int wb, int nb) {
   const int G = decode_grid(f);
   const int nch = d * wb / 16;
   const size_t rpg = (size_t)decode_rows_side_by_side(nch);
-  size_t bytes = sizeof(Ctrl);
+  size_t bytes = kWsHeader;
   bytes += (size_t)G * kBMaxAll * sizeof(int32_t);
   bytes = (bytes + 255) & ~(size_t)255;
   bytes += (size_t)kBMaxAll * f * sizeof(int32_t);
@@ -466,7 +472,7 @@ size_t decode_workspace_bytes(int d, int f, int wb, int nb) {
 void decode_carve(DecodeArgs& a, void* ws, int wb) {
   char* p = static_cast<char*>(ws);
   a.ctrl = reinterpret_cast<Ctrl*>(p);
-  size_t off = sizeof(Ctrl);
+  size_t off = kWsHeader;
   a.tile_cnt = reinterpret_cast<int32_t*>(p + off);
   off += (size_t)a.G * kBMaxAll * sizeof(int32_t);
   off = (off + 255) & ~(size_t)255;

@@ -175,6 +175,7 @@ __global__ __launch_bounds__(256) void chunk_stage2_kernel(const uint16_t* __res
     const uint32_t old = __hip_atomic_fetch_add(&arrive[ct], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (old == (uint32_t)(S - 1)) ? 1u : 0u;
     if (s_last) __hip_atomic_store(&arrive[ct], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // old >= S means the counter was not zero at launch; no tile is then summed
   }
   __syncthreads();
   if (!s_last) return;
@@ -205,10 +206,8 @@ size_t chunk_workspace_bytes(int d, int f, int wdtype, int n) {
     // fp32 weights run through the decode kernel, 4 tokens at a time
     return decode_workspace_bytes(d, f, 4, n > 1 ? 4 : 1);
   }
-  const int ntile = (d + kColTile - 1) / kColTile;
   const int S = chunk_splits(d, f);
-  size_t bytes = (size_t)ntile * sizeof(uint32_t);
-  bytes = (bytes + 255) & ~(size_t)255;
+  size_t bytes = kWsHeader;
   bytes += (size_t)SFN_MAX_CHUNK * ((f + 7) & ~7) * sizeof(uint16_t);
   bytes = (bytes + 255) & ~(size_t)255;
   bytes += (size_t)S * SFN_MAX_CHUNK * d * sizeof(float);
@@ -244,10 +243,10 @@ hipError_t launch_dense_chunk(const sfn_ffn& ffn, const void* x, int n, float* y
   }
   const int ntile = (ffn.d + kColTile - 1) / kColTile;
   const int S = chunk_splits(ffn.d, ffn.f);
+  if (ntile > kMaxColTiles) return hipErrorInvalidValue;
   char* p = static_cast<char*>(ws);
-  uint32_t* arrive = reinterpret_cast<uint32_t*>(p);
-  size_t off = (size_t)ntile * sizeof(uint32_t);
-  off = (off + 255) & ~(size_t)255;
+  uint32_t* arrive = reinterpret_cast<uint32_t*>(p + kWsChunkCounters);
+  size_t off = kWsHeader;
   uint16_t* H = reinterpret_cast<uint16_t*>(p + off);
   off += (size_t)SFN_MAX_CHUNK * ((ffn.f + 7) & ~7) * sizeof(uint16_t);
   off = (off + 255) & ~(size_t)255;

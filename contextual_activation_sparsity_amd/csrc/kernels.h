@@ -9,8 +9,18 @@
 
 namespace sfn {
 
-// Control words at the start of every workspace (zero-filled once by the caller; every
-// call leaves them as it found them except the monotonically increasing release word).
+// Workspace layout shared by every call on a workspace:
+//   [0, 256)            decode control words (Ctrl)
+//   [256, 1280)         dense-chunk column-tile arrival counters (256 x uint32)
+//   [1280, kWsHeader)   reserved
+//   [kWsHeader, ...)    per-call scratch, rewritten by each call before it is read
+// The header is zero-filled once by the caller; each call leaves its counters at zero
+// (the decode release word only ever increases). Scratch of one call may overlap scratch
+// of another, never the header.
+constexpr size_t kWsHeader = 2048;
+constexpr size_t kWsChunkCounters = 256;
+constexpr int kMaxColTiles = 256;
+
 struct Ctrl {
   uint32_t arrive;   // workgroups that finished their partial in the current launch
   uint32_t release;  // bumped by the last arriving workgroup

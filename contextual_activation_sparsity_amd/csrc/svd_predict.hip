@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void svd_p_kernel(const char* __restrict__ l, 
 size_t svd_workspace_bytes(int d, int f, int r) {
   (void)d;
   const int ntiles = (f + kRowsPerTile - 1) / kRowsPerTile;
-  size_t bytes = sizeof(SvdWs);
+  size_t bytes = kWsHeader + sizeof(SvdWs);
   bytes += (size_t)ntiles * sizeof(unsigned long long);
   bytes = (bytes + 255) & ~(size_t)255;
   bytes += (size_t)r * sizeof(float);
@@ -157,7 +157,7 @@ size_t svd_workspace_bytes(int d, int f, int r) {
 hipError_t launch_svd_predict(const sfn_svd& s, const void* x, int32_t* cand, int32_t* n_cand, float* p_out,
                               void* ws, hipStream_t stream) {
   const int ntiles = (s.f + kRowsPerTile - 1) / kRowsPerTile;
-  char* p = static_cast<char*>(ws);
+  char* p = static_cast<char*>(ws) + kWsHeader;
   SvdWs* st = reinterpret_cast<SvdWs*>(p);
   unsigned long long* flags = reinterpret_cast<unsigned long long*>(p + sizeof(SvdWs));
   size_t off = sizeof(SvdWs) + (size_t)ntiles * sizeof(unsigned long long);

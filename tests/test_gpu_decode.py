@@ -212,3 +212,55 @@ def test_candidate_mode_reglu():
             assert normwise_err(y[0], y_own) <= TOL_BF16
         else:
             assert np.all(y[0] == 0.0)
+
+
+def test_one_workspace_shared_by_every_call():
+    """calibrate -> decode -> dense chunk -> predictor -> decode -> calibrate -> decode on a
+    single workspace: each call must leave the persistent control words as it found them
+    (regression: the calibration state used to overlap the decode arrival counter)."""
+    w = inputs.workload(1)
+    d, f, n_cal = 2048, 3000, 64
+    raw, dev, host = swiglu_layer_dev(w, 0, d=d, f=f)
+    Wg, Wu, Dt = host["w_gate"], host["w_up"], host["w_down_t"]
+    layer = B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"])
+    Q, L = oracle.svd_factors(Wg, 64)
+    Qb, Lb = inputs.f32_to_bf16_bits(Q), inputs.f32_to_bf16_bits(L)
+    pred = B.SVDPredictor(to_dev(Qb, "bf16"), to_dev(Lb, "bf16"), torch.zeros(f, dtype=torch.float32, device="cuda"))
+    ws = B.workspace(max(B.sparse_ffn_workspace_size(layer, n_cal), B.svd_predict_workspace_size(pred)))
+    xcal_raw = inputs.tokens(w, n_cal, inputs.STREAM_CAL, d=d)
+    xs_raw = inputs.tokens(w, 3, inputs.STREAM_DECODE, d=d)
+    xs = to_f64(xs_raw, "bf16")
+    t_dev = torch.empty(1, dtype=torch.float32, device="cuda")
+
+    def decode_check(j):
+        y = torch.empty((1, d), dtype=torch.float32, device="cuda")
+        idx = torch.empty((1, f), dtype=torch.int32, device="cuda")
+        n_act = torch.empty(1, dtype=torch.int32, device="cuda")
+        B.sparse_ffn_decode(layer, to_dev(xs_raw[j:j + 1], "bf16"), t_dev, ws, y=y, active_idx=idx, n_active=n_act)
+        torch.cuda.synchronize()
+        assert _ctrl_error(ws) == 0
+        t = float(t_dev.item())
+        gm = mask_from_idx(idx.cpu().numpy()[0], int(n_act.item()), f)
+        om, oa, _ = oracle.cats_decode(Wg, Wu, Dt, xs[j][None], t)
+        check_mask(gm, om[0], np.abs(oa[0]), t)
+        assert normwise_err(y.cpu().numpy()[0], oracle.masked_ffn(Wg, Wu, Dt, xs[j], gm)) <= TOL_BF16
+
+    say("[shared ws] calibrate, decode")
+    B.sparse_ffn_calibrate(layer, to_dev(xcal_raw, "bf16"), 0.5, t_dev, ws)
+    decode_check(0)
+    say("[shared ws] dense chunk")
+    yc = torch.empty((3, d), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        B.ffn_dense_chunk(layer, to_dev(xs_raw, "bf16"), yc, ws)
+        torch.cuda.synchronize()
+        Yo = oracle.dense_chunk(Wg, Wu, Dt, xs)
+        for j in range(3):
+            assert normwise_err(yc.cpu().numpy()[j], Yo[j]) <= TOL_BF16
+    say("[shared ws] predictor, decode")
+    cand = torch.empty(f, dtype=torch.int32, device="cuda")
+    n_cand = torch.empty(1, dtype=torch.int32, device="cuda")
+    B.svd_predict(pred, to_dev(xs_raw[1], "bf16"), cand, n_cand, ws)
+    decode_check(1)
+    say("[shared ws] calibrate again, decode")
+    B.sparse_ffn_calibrate(layer, to_dev(xcal_raw, "bf16"), 0.7, t_dev, ws)
+    decode_check(2)
