@@ -50,91 +50,158 @@ struct StepDesc {
   int n;     // rows in the step
 };
 
+// The kernel's view of DecodeArgs: the same fields with global-address-space pointers,
+// held in registers (built from the by-value argument at kernel entry).
+struct DevArgs {
+  const SFN_GLOBAL char* wg;
+  const SFN_GLOBAL char* wu;
+  const SFN_GLOBAL char* wd;
+  const SFN_GLOBAL float* bias;
+  const SFN_GLOBAL char* x;
+  const SFN_GLOBAL float* t;
+  const SFN_GLOBAL int32_t* cand;
+  const SFN_GLOBAL int32_t* n_cand;
+  const SFN_GLOBAL uint8_t* mask_in;
+  SFN_GLOBAL float* y;
+  SFN_GLOBAL int32_t* active_idx;
+  SFN_GLOBAL int32_t* n_active;
+  SFN_GLOBAL Ctrl* ctrl;
+  SFN_GLOBAL int32_t* tile_cnt;
+  SFN_GLOBAL int32_t* tile_idx;
+  SFN_GLOBAL float* part;
+  int d, f, nch, row_bytes, nb, act, G, n_red;
+};
+
+__device__ __forceinline__ DevArgs dev_args(const DecodeArgs& h) {
+  DevArgs a;
+  a.wg = gp(h.wg); a.wu = gp(h.wu); a.wd = gp(h.wd); a.bias = gp(h.bias); a.x = gp(h.x); a.t = gp(h.t);
+  a.cand = gp(h.cand); a.n_cand = gp(h.n_cand); a.mask_in = gp(h.mask_in); a.y = gp(h.y);
+  a.active_idx = gp(h.active_idx); a.n_active = gp(h.n_active); a.ctrl = gp(h.ctrl);
+  a.tile_cnt = gp(h.tile_cnt); a.tile_idx = gp(h.tile_idx); a.part = gp(h.part);
+  a.d = h.d; a.f = h.f; a.nch = h.nch; a.row_bytes = h.row_bytes; a.nb = h.nb; a.act = h.act; a.G = h.G;
+  a.n_red = h.n_red;
+  return a;
+}
+
+// Zero words that stand in for absent optional inputs, so that every step issues the
+// same loads whatever it holds.
+__device__ __attribute__((aligned(16))) float g_zero_f32[4];
+__device__ __attribute__((aligned(16))) uint8_t g_zero_u8[16];
+
 template <int WT, int BMAX, int CPT, int TPR, int R>
 struct DecodeKernel {
   using CK = Chunk<WT>;
   static constexpr int RPG = kNT / TPR;  // rows processed side by side
-  static constexpr int RG = RPG * R;     // rows per step
-  static constexpr int V = R * BMAX;     // values each thread reduces per step
+  static constexpr int RG = RPG * R;     // rows of an up/down step (and of half a gate step)
+  static constexpr int RS = 2 * RG;      // rows of a gate step
+  static constexpr int VG = 2 * R * BMAX;
+  static constexpr int VU = R * BMAX;
   static constexpr int WPR = TPR / 64;   // waves per row
   static constexpr int KV = CK::kVals;
-  static_assert(RG <= 64, "one lane of wave 0 per row of a step");
-  static_assert((V & (V - 1)) == 0 && V <= 64, "power-of-two value count");
+  static_assert(RS <= 64, "one lane of wave 0 per row of a gate step");
+  static_assert((VG & (VG - 1)) == 0 && VG <= 64, "power-of-two value count");
 
   struct Smem {
-    int rowid[kTMax];            // candidate mode: global row of each local row
-    float aval[kTMax][BMAX];     // activation per local row and token
-    uint8_t mbits[kTMax];        // bit b: token b active
-    int queue[kTMax];            // local rows active for some token, ascending
-    float wpart[kNW][V];         // per-wave partial sums of a step
-    float h[64][BMAX];           // h = m a u of the rows of an up/down step
-    float red[kNT];              // reducer scratch
-    int pref[1025];              // tile prefix (index output)
+    int rowid[kTMax];         // candidate mode: global row of each local row
+    float aval[kTMax][BMAX];  // activation per local row and token
+    uint8_t mbits[kTMax];     // bit b: token b active
+    int queue[kTMax];         // local rows active for some token, ascending
+    float wpart[kNW][VG];     // per-wave partial sums of a step
+    float h[64][BMAX];        // h = m a u of the rows of an up/down step
+    float red[kNT];           // reducer scratch
+    int pref[1025];           // tile prefix (index output)
     int qlen;
     int cnt[BMAX];
     uint32_t ticket;
     uint32_t rel0;
   };
 
-  // Loads of one step: gate rows into w0, or Wu rows into w0 and Dt rows into w1.
-  __device__ __forceinline__ static void issue(const DecodeArgs& a, const Smem& sm, const StepDesc& sd,
-                                               int r0, bool cand_mode, int rl, int cl,
-                                               uint4 (&w0)[R][CPT], uint4 (&w1)[R][CPT]) {
-    if (sd.kind == STEP_NONE) return;
+  // Loads of one step into a buffer. The instruction stream is the same for every kind
+  // of step (only addresses differ), so the compiler can count the loads in flight and
+  // wait for exactly the older buffer:
+  //   gate:    w0 = Wg rows [base, base+RG), w1 = Wg rows [base+RG, base+RS)
+  //   up/down: w0 = Wu rows, w1 = Dt rows of queue entries [base, base+n)
+  //   none:    both from x (L1-resident), results unused
+  // Rows past the end are clamped to a valid row; their results are masked later.
+  // Each lane also fetches the bias and mask bytes of gate row (lane % RS).
+  __device__ __forceinline__ static void issue(const DevArgs& a, const Smem& sm, const StepDesc& sd, int r0,
+                                               int nrows, bool cand_mode, int rl, int cl, int lane,
+                                               uint4 (&w0)[R][CPT], uint4 (&w1)[R][CPT], float& bias,
+                                               uint32_t (&mraw)[BMAX], uint32_t& valid) {
+    const bool gate = sd.kind == STEP_GATE, upd = sd.kind == STEP_UPDOWN;
+    const SFN_GLOBAL char* p0 = gate ? a.wg : (upd ? a.wu : a.x);
+    const SFN_GLOBAL char* p1 = gate ? a.wg : (upd ? a.wd : a.x);
+    const size_t rb = (sd.kind == STEP_NONE) ? 0 : (size_t)a.row_bytes;
+    const int lrmax = nrows > 0 ? nrows - 1 : 0;
+    valid = 0;
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const int j = rl + RPG * k;
-      const bool valid = j < sd.n;
-      int grow = 0;
-      if (valid) {
-        const int lr = (sd.kind == STEP_GATE) ? sd.base + j : sm.queue[sd.base + j];
-        grow = cand_mode ? sm.rowid[lr] : r0 + lr;
+      int lr0, lr1;
+      bool v0, v1;
+      if (gate) {
+        lr0 = sd.base + j;
+        lr1 = sd.base + RG + j;
+        v0 = lr0 < nrows;
+        v1 = lr1 < nrows;
+      } else {
+        v0 = v1 = upd && j < sd.n;
+        lr0 = lr1 = sm.queue[min(sd.base + j, kTMax - 1)];
       }
-      const size_t roff = (size_t)grow * (size_t)a.row_bytes;
+      lr0 = min(max(lr0, 0), lrmax);
+      lr1 = min(max(lr1, 0), lrmax);
+      const int g0 = cand_mode ? sm.rowid[lr0] : r0 + lr0;
+      const int g1 = cand_mode ? sm.rowid[lr1] : r0 + lr1;
+      valid |= (uint32_t)v0 << k;
+      valid |= (uint32_t)v1 << (R + k);
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        const int ch = cl + TPR * c;
-        const bool ok = valid && ch < a.nch;
-        if (sd.kind == STEP_GATE) {
-          w0[k][c] = ok ? ldg16(a.wg + roff + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
-        } else {
-          w0[k][c] = ok ? ldg16(a.wu + roff + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
-          w1[k][c] = ok ? ldg16(a.wd + roff + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
-        }
+        int ch = cl + TPR * c;
+        ch = ch < a.nch ? ch : 0;
+        w0[k][c] = ldg16(p0 + (size_t)g0 * rb + (size_t)ch * 16);
+        w1[k][c] = ldg16(p1 + (size_t)g1 * rb + (size_t)ch * 16);
       }
+    }
+    // bias and mask bytes of gate row (lane % RS) of this step
+    int lb = gate ? sd.base + (lane % RS) : 0;
+    lb = min(max(lb, 0), lrmax);
+    const int gb = cand_mode ? sm.rowid[lb] : r0 + lb;
+    bias = a.bias ? a.bias[gb] : gp(g_zero_f32)[0];
+    // raw bytes: tested only when the step is processed, so no wait is forced here
+#pragma unroll
+    for (int b = 0; b < BMAX; ++b) {
+      const int bb = b < a.nb ? b : 0;
+      mraw[b] = a.mask_in ? a.mask_in[(size_t)bb * a.f + gb] : gp(g_zero_u8)[b];
     }
   }
 
-  // Dot products of the step's rows with the tokens, reduced to per-wave partials.
-  __device__ __forceinline__ static void dots_to_lds(Smem& sm, const uint4 (&w)[R][CPT],
-                                                     const uint4 (&xr)[BMAX][CPT]) {
-    float s[V];
-#pragma unroll
-    for (int k = 0; k < R; ++k)
-#pragma unroll
-      for (int b = 0; b < BMAX; ++b) {
-        float acc = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) acc = CK::dot(w[k][c], xr[b][c], acc);
-        s[k * BMAX + b] = acc;
-      }
-    wave_transpose_sum<V>(s);
+  // Wave totals of NV values per thread into sm.wpart[wave][0..NV): blocks of up to 16
+  // values are transposed and summed across the wave, then written by one lane each.
+  template <int NV>
+  __device__ __forceinline__ static void reduce_to_lds(Smem& sm, float (&s)[NV]) {
+    constexpr int BLK = NV < 16 ? NV : 16;
+    constexpr int LOGB = (BLK >= 16) ? 4 : (BLK >= 8) ? 3 : (BLK >= 4) ? 2 : (BLK >= 2) ? 1 : 0;
+    constexpr int SH = 6 - LOGB;
     const int lane = threadIdx.x & 63;
-    constexpr int LOGV = (V >= 64) ? 6 : (V >= 32) ? 5 : (V >= 16) ? 4 : (V >= 8) ? 3 : (V >= 4) ? 2 : (V >= 2) ? 1 : 0;
-    constexpr int SH = 6 - LOGV;
-    if ((lane & ((1 << SH) - 1)) == 0) sm.wpart[threadIdx.x >> 6][lane >> SH] = s[0];
+#pragma unroll
+    for (int blk = 0; blk < NV / BLK; ++blk) {
+      float t[BLK];
+#pragma unroll
+      for (int i = 0; i < BLK; ++i) t[i] = s[blk * BLK + i];
+      wave_transpose_sum<BLK>(t);
+      if ((lane & ((1 << SH) - 1)) == 0) sm.wpart[threadIdx.x >> 6][blk * BLK + (lane >> SH)] = t[0];
+    }
   }
 
-  // Sum of the wave partials of row j (0 <= j < RG) of a step, token b.
-  __device__ __forceinline__ static float row_sum(const Smem& sm, int j, int b) {
-    const int rlj = j % RPG, k = j / RPG;
+  __device__ __forceinline__ static float wave_partial_sum(const Smem& sm, int rlj, int v) {
     float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < WPR; ++i) acc += sm.wpart[rlj * WPR + i][k * BMAX + b];
+    for (int i = 0; i < WPR; ++i) acc += sm.wpart[rlj * WPR + i][v];
     return acc;
   }
 
-  __device__ static void run(const DecodeArgs& a) {
+  __device__ static void run(const DecodeArgs& args) {
+    const DevArgs a = dev_args(args);
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rl = tid / TPR, cl = tid % TPR;
@@ -178,16 +245,17 @@ struct DecodeKernel {
         for (int v = 0; v < KV; ++v) acc[b][c][v] = 0.f;
     __syncthreads();
 
-    // ---- software-pipelined steps
-    const int ngate = (nrows + RG - 1) / RG;
+    // ---- software-pipelined steps (one issued ahead of the one processed)
+    const int ngate = (nrows + RS - 1) / RS;
     int next_gate = 0;  // gate steps issued
+    int gates_done = 0; // gate steps processed
     int qh = 0;         // queue rows handed to up/down steps
     auto next_step = [&]() -> StepDesc {
       StepDesc sd{STEP_NONE, 0, 0};
       if (next_gate < ngate) {
         sd.kind = STEP_GATE;
-        sd.base = next_gate * RG;
-        sd.n = min(RG, nrows - sd.base);
+        sd.base = next_gate * RS;
+        sd.n = min(RS, nrows - sd.base);
         ++next_gate;
       } else if (want_y) {
         const int ql = sm.qlen;
@@ -201,27 +269,42 @@ struct DecodeKernel {
       return sd;
     };
 
-    auto process = [&](const StepDesc& sd, const uint4 (&w0)[R][CPT], const uint4 (&w1)[R][CPT]) {
-      dots_to_lds(sm, w0, xr);
-      __syncthreads();
+    auto process = [&](const StepDesc& sd, const uint4 (&w0)[R][CPT], const uint4 (&w1)[R][CPT], float bias,
+                       const uint32_t (&mraw)[BMAX], uint32_t valid) {
       if (sd.kind == STEP_GATE) {
+        float s[VG];
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+#pragma unroll
+          for (int b = 0; b < BMAX; ++b) {
+            float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+              d0 = CK::dot(w0[k][c], xr[b][c], d0);
+              d1 = CK::dot(w1[k][c], xr[b][c], d1);
+            }
+            s[k * BMAX + b] = d0;
+            s[(R + k) * BMAX + b] = d1;
+          }
+        reduce_to_lds<VG>(sm, s);
+        __syncthreads();
         if (wave == 0) {
+          // lane j finalizes row j of the step: half h = j / RG, row-lane j % RPG, slot k
           const int j = lane;
-          const bool valid = j < sd.n;
+          const int hh = j / RG, jj = j % RG;
+          const int rlj = jj % RPG, k = jj / RPG;
+          const bool ok = j < sd.n;
           const int lr = sd.base + j;
           uint32_t bits = 0;
           int grow = 0;
-          if (valid) {
+          if (ok) {
             grow = cand_mode ? sm.rowid[lr] : r0 + lr;
-            const float bias = a.bias ? a.bias[grow] : 0.f;
 #pragma unroll
             for (int b = 0; b < BMAX; ++b) {
               if (b < nb) {
-                const float g = row_sum(sm, j, b) + bias;
+                const float g = wave_partial_sum(sm, rlj, (hh * R + k) * BMAX + b) + bias;
                 const float av = (a.act == 0) ? silu_f(g) : fmaxf(g, 0.f);
-                bool on;
-                if (a.mask_in) on = a.mask_in[(size_t)b * a.f + grow] != 0;
-                else on = fabsf(av) > thr;
+                const bool on = a.mask_in ? mraw[b] != 0u : fabsf(av) > thr;
                 sm.aval[lr][b] = av;
                 bits |= (uint32_t)on << b;
               }
@@ -240,7 +323,9 @@ struct DecodeKernel {
                 const unsigned long long bb = __ballot(on);
                 const int pb = __builtin_amdgcn_mbcnt_hi((uint32_t)(bb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bb, 0));
                 const int c0 = sm.cnt[b];
-                if (on) a.tile_idx[(size_t)b * a.f + r0 + c0 + pb] = grow;
+                if (on)
+                  __hip_atomic_store(&a.tile_idx[(size_t)b * a.f + r0 + c0 + pb], grow, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
                 if (lane == 0) sm.cnt[b] = c0 + __popcll(bb);
               }
             }
@@ -248,21 +333,35 @@ struct DecodeKernel {
           if (lane == 0) sm.qlen = q0 + __popcll(ub);
         }
         __syncthreads();
-      } else {
+        ++gates_done;
+      } else if (sd.kind == STEP_UPDOWN) {
+        float s[VU];
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+#pragma unroll
+          for (int b = 0; b < BMAX; ++b) {
+            float d0 = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) d0 = CK::dot(w0[k][c], xr[b][c], d0);
+            s[k * BMAX + b] = d0;
+          }
+        reduce_to_lds<VU>(sm, s);
+        __syncthreads();
         if (wave == 0 && lane < sd.n) {
           const int lr = sm.queue[sd.base + lane];
           const uint32_t bits = sm.mbits[lr];
+          const int rlj = lane % RPG, k = lane / RPG;
 #pragma unroll
           for (int b = 0; b < BMAX; ++b) {
-            const float u = row_sum(sm, lane, b);
+            const float u = wave_partial_sum(sm, rlj, k * BMAX + b);
             sm.h[lane][b] = ((bits >> b) & 1u) ? sm.aval[lr][b] * u : 0.f;
           }
         }
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < R; ++k) {
-          const int j = rl + RPG * k;
-          if (j < sd.n) {
+          if ((valid >> (R + k)) & 1u) {
+            const int j = rl + RPG * k;
 #pragma unroll
             for (int b = 0; b < BMAX; ++b) {
               const float hv = sm.h[j][b];
@@ -275,30 +374,24 @@ struct DecodeKernel {
     };
 
     uint4 a0[R][CPT], a1[R][CPT], b0[R][CPT], b1[R][CPT];
-    StepDesc da = next_step();
-    issue(a, sm, da, r0, cand_mode, rl, cl, a0, a1);
-    while (da.kind != STEP_NONE) {
-      StepDesc db = next_step();
-      issue(a, sm, db, r0, cand_mode, rl, cl, b0, b1);
-      process(da, a0, a1);
-      if (db.kind == STEP_NONE) {
-        db = next_step();
-        issue(a, sm, db, r0, cand_mode, rl, cl, b0, b1);
-      }
-      if (db.kind == STEP_NONE) break;
-      StepDesc dn = next_step();
-      issue(a, sm, dn, r0, cand_mode, rl, cl, a0, a1);
-      process(db, b0, b1);
-      if (dn.kind == STEP_NONE) {
-        dn = next_step();
-        issue(a, sm, dn, r0, cand_mode, rl, cl, a0, a1);
-      }
-      da = dn;
+    float abias, bbias;
+    uint32_t amask[BMAX], bmask[BMAX], avalid, bvalid;
+    StepDesc sa = next_step();
+    issue(a, sm, sa, r0, nrows, cand_mode, rl, cl, lane, a0, a1, abias, amask, avalid);
+    while (true) {
+      StepDesc sb = next_step();
+      issue(a, sm, sb, r0, nrows, cand_mode, rl, cl, lane, b0, b1, bbias, bmask, bvalid);
+      process(sa, a0, a1, abias, amask, avalid);
+      if (sa.kind == STEP_NONE && sb.kind == STEP_NONE && gates_done == ngate && (!want_y || qh == sm.qlen)) break;
+      sa = next_step();
+      issue(a, sm, sa, r0, nrows, cand_mode, rl, cl, lane, a0, a1, abias, amask, avalid);
+      process(sb, b0, b1, bbias, bmask, bvalid);
+      if (sa.kind == STEP_NONE && sb.kind == STEP_NONE && gates_done == ngate && (!want_y || qh == sm.qlen)) break;
     }
 
-    // ---- partial of y and the tile's index counts
+    // ---- partial of y (device-coherent stores: read by other workgroups below)
     if (want_y) {
-      float* prow = a.part + ((size_t)(w * RPG + rl) * nb) * a.d;
+      SFN_GLOBAL float* prow = a.part + ((size_t)(w * RPG + rl) * nb) * a.d;
 #pragma unroll
       for (int b = 0; b < BMAX; ++b) {
         if (b < nb) {
@@ -306,23 +399,30 @@ struct DecodeKernel {
           for (int c = 0; c < CPT; ++c) {
             const int ch = cl + TPR * c;
             if (ch < a.nch) {
-              float* dst = prow + (size_t)b * a.d + (size_t)ch * KV;
+              SFN_GLOBAL float* dst = prow + (size_t)b * a.d + (size_t)ch * KV;
 #pragma unroll
-              for (int v = 0; v < KV; v += 4)
-                *reinterpret_cast<float4*>(dst + v) = make_float4(acc[b][c][v], acc[b][c][v + 1], acc[b][c][v + 2], acc[b][c][v + 3]);
+              for (int v = 0; v < KV; ++v)
+                __hip_atomic_store(dst + v, acc[b][c][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
           }
         }
       }
     }
-    if (want_idx && tid < kBMaxAll) a.tile_cnt[w * kBMaxAll + tid] = (tid < BMAX) ? sm.cnt[tid] : 0;
+    if (want_idx && tid < kBMaxAll)
+      __hip_atomic_store(&a.tile_cnt[w * kBMaxAll + tid], (tid < BMAX) ? sm.cnt[tid] : 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
 
-    // ---- arrival; the last n_red workgroups reduce
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // ---- arrival; the last n_red workgroups reduce.
+    // No cache-maintenance fences: the partials above are device-scope stores that write
+    // through to the coherent level, s_waitcnt 0 waits until every one of them is
+    // acknowledged, and the readers use device-scope loads. (An agent-scope release or
+    // acquire fence would write back or invalidate the whole L2 of the XCD.)
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
       sm.rel0 = __hip_atomic_load(&a.ctrl->release, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      sm.ticket = __hip_atomic_fetch_add(&a.ctrl->arrive, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+      sm.ticket = __hip_atomic_fetch_add(&a.ctrl->arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     const uint32_t ticket = sm.ticket;
@@ -337,13 +437,14 @@ struct DecodeKernel {
     if (tid == 0) {
       if (ticket == (uint32_t)(a.G - 1)) {
         __hip_atomic_store(&a.ctrl->arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(&a.ctrl->release, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        __hip_atomic_fetch_add(&a.ctrl->release, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {
         const uint32_t r0v = sm.rel0;
         uint32_t spins = 0;
-        while (__hip_atomic_load(&a.ctrl->release, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == r0v) {
-          __builtin_amdgcn_s_sleep(2);
-          if (++spins > (1u << 22)) {
+        while (__hip_atomic_load(&a.ctrl->release, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == r0v) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > (1u << 24)) {
             __hip_atomic_store(&a.ctrl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
           }
@@ -351,7 +452,6 @@ struct DecodeKernel {
       }
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int ri = (int)(ticket - first_red);
 
     if (want_y) {
@@ -365,8 +465,20 @@ struct DecodeKernel {
         const int npg = kNT / slmax;
         const int e = tid % slmax, pg = tid / slmax;
         float sum = 0.f;
-        if (pg < npg && e < SL)
-          for (int p = pg; p < P; p += npg) sum += a.part[(size_t)p * L + s0 + e];
+        if (pg < npg && e < SL) {
+          const SFN_GLOBAL float* src = a.part + s0 + e;
+          int p = pg;
+          // eight device-scope loads in flight, summed in partial order
+          for (; p + 7 * npg < P; p += 8 * npg) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              v[u] = __hip_atomic_load(src + (size_t)(p + u * npg) * L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sum += v[u];
+          }
+          for (; p < P; p += npg) sum += __hip_atomic_load(src + (size_t)p * L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         sm.red[tid] = sum;
         __syncthreads();
         if (pg == 0 && e < SL) {
@@ -377,7 +489,8 @@ struct DecodeKernel {
       } else {
         for (int e = tid; e < SL; e += kNT) {
           float sum = 0.f;
-          for (int p = 0; p < P; ++p) sum += a.part[(size_t)p * L + s0 + e];
+          for (int p = 0; p < P; ++p)
+            sum += __hip_atomic_load(a.part + (size_t)p * L + s0 + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           a.y[s0 + e] = sum;
         }
       }
@@ -389,7 +502,10 @@ struct DecodeKernel {
       for (int b = 0; b < nb; ++b) {
         __syncthreads();
         // exclusive prefix of the tile counts, tiles in row order
-        for (int i = tid; i <= a.G; i += kNT) sm.pref[i] = (i < a.G) ? a.tile_cnt[i * kBMaxAll + b] : 0;
+        for (int i = tid; i <= a.G; i += kNT)
+          sm.pref[i] = (i < a.G) ? __hip_atomic_load(&a.tile_cnt[i * kBMaxAll + b], __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0;
         __syncthreads();
         if (tid == 0) {
           int run = 0;
@@ -405,7 +521,8 @@ struct DecodeKernel {
             const int tr0 = (int)((long long)tile * n_total / a.G);
             const int c = sm.pref[tile + 1] - sm.pref[tile];
             for (int i = lane; i < c; i += 64)
-              a.active_idx[(size_t)b * a.f + sm.pref[tile] + i] = a.tile_idx[(size_t)b * a.f + tr0 + i];
+              a.active_idx[(size_t)b * a.f + sm.pref[tile] + i] =
+                  __hip_atomic_load(&a.tile_idx[(size_t)b * a.f + tr0 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
         if (tid == 0 && a.n_active) a.n_active[b] = sm.pref[a.G];
@@ -421,14 +538,17 @@ __global__ __launch_bounds__(kNT) void decode_kernel(DecodeArgs a) {
 
 template <int WT, int BMAX>
 hipError_t dispatch_tpr(const DecodeArgs& a, hipStream_t s) {
+  // rows per thread per half step: 16 weight loads in flight per thread and buffer for
+  // one token, 8 for four tokens (the dot-product registers grow with the batch)
+  constexpr int RB = BMAX == 1 ? 8 : 4;
   const dim3 grid(a.G), block(kNT);
   if (a.nch > 2048) return hipErrorInvalidValue;
-  if (a.nch > 1024) { hipLaunchKernelGGL((decode_kernel<WT, BMAX, 4, 512, 2>), grid, block, 0, s, a); }
-  else if (a.nch > 512) { hipLaunchKernelGGL((decode_kernel<WT, BMAX, 2, 512, 4>), grid, block, 0, s, a); }
-  else if (a.nch > 256) { hipLaunchKernelGGL((decode_kernel<WT, BMAX, 1, 512, 8>), grid, block, 0, s, a); }
-  else if (a.nch > 128) { hipLaunchKernelGGL((decode_kernel<WT, BMAX, 1, 256, 4>), grid, block, 0, s, a); }
-  else if (a.nch > 64) { hipLaunchKernelGGL((decode_kernel<WT, BMAX, 1, 128, 8>), grid, block, 0, s, a); }
-  else { hipLaunchKernelGGL((decode_kernel<WT, BMAX, 1, 64, 8>), grid, block, 0, s, a); }
+  if (a.nch > 1024) { hipLaunchKernelGGL((decode_kernel<WT, BMAX, 4, 512, RB / 4>), grid, block, 0, s, a); }
+  else if (a.nch > 512) { hipLaunchKernelGGL((decode_kernel<WT, BMAX, 2, 512, RB / 2>), grid, block, 0, s, a); }
+  else if (a.nch > 256) { hipLaunchKernelGGL((decode_kernel<WT, BMAX, 1, 512, RB>), grid, block, 0, s, a); }
+  else if (a.nch > 128) { hipLaunchKernelGGL((decode_kernel<WT, BMAX, 1, 256, RB>), grid, block, 0, s, a); }
+  else if (a.nch > 64) { hipLaunchKernelGGL((decode_kernel<WT, BMAX, 1, 128, RB>), grid, block, 0, s, a); }
+  else { hipLaunchKernelGGL((decode_kernel<WT, BMAX, 1, 64, 4>), grid, block, 0, s, a); }
   return hipGetLastError();
 }
 

@@ -61,12 +61,26 @@ struct Chunk<WT_F32> {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
+// Global-address-space pointers. Pointers that arrive inside a by-value argument struct
+// are generic; accessing through them would emit flat instructions, which count against
+// the LDS wait counter too and serialize LDS waits behind every weight load in flight.
+#define SFN_GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ SFN_GLOBAL T* gp(T* p) {
+  return (SFN_GLOBAL T*)p;
+}
+
 // 16-byte streaming load (weights are read once per call: non-temporal hint).
-__device__ __forceinline__ uint4 ldg16(const char* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+__device__ __forceinline__ uint4 ldg16(const SFN_GLOBAL char* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const SFN_GLOBAL u32x4_t*>(p));
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
-__device__ __forceinline__ uint4 ld16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint4 ld16(const SFN_GLOBAL char* p) {
+  const u32x4_t v = *reinterpret_cast<const SFN_GLOBAL u32x4_t*>(p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint4 ldg16(const char* p) { return ldg16(gp(p)); }
+__device__ __forceinline__ uint4 ld16(const char* p) { return ld16(gp(p)); }
 
 // ---- cross-lane moves (wave64) ------------------------------------------------------
 // DPP controls: quad_perm [1,0,3,2] swaps lane pairs, [2,3,0,1] swaps pairs of pairs,
@@ -94,46 +108,66 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Lane select for the halving steps: hi in the lanes whose index has bit BIT set, lo in
+// the others, for BIT in {32, 16, 8, 4}. A DPP identity move whose row mask (lane groups
+// of 16) or bank mask (groups of 4 inside a row) enables only those lanes writes hi there
+// and leaves lo elsewhere. (A ternary on array elements can turn into a dynamically
+// indexed, scratch-backed array; DPP keeps it a register operation the compiler sees.)
+template <int BIT>
+__device__ __forceinline__ float sel_upper(float lo, float hi) {
+  static_assert(BIT == 32 || BIT == 16 || BIT == 8 || BIT == 4, "row/bank granularity");
+  constexpr int ROW = BIT == 32 ? 0xC : BIT == 16 ? 0xA : 0xF;
+  constexpr int BANK = BIT == 8 ? 0xC : BIT == 4 ? 0xA : 0xF;
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(lo), __float_as_int(hi), 0xE4 /* identity */,
+                                                    ROW, BANK, false));
+}
+
+// One halving step over lane bit BIT: values [0, H) stay, values [H, 2H) are exchanged,
+// so that afterwards slot i holds value i (lanes without BIT) or i + H (lanes with it),
+// summed with the partner lane l ^ BIT.
+template <int BIT, int H>
+__device__ __forceinline__ void halve_step(float* s) {
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float lo = s[i], hi = s[i + H];
+    const float keep = sel_upper<BIT>(lo, hi);
+    const float send = sel_upper<BIT>(hi, lo);
+    s[i] = keep + shfl_xor_f(send, BIT);
+  }
+}
+
+template <int BIT>
+__device__ __forceinline__ float lane_pair_sum(float v) {
+  if constexpr (BIT >= 16) return v + shfl_xor_f(v, BIT);
+  else if constexpr (BIT == 8) return v + dpp_mov<SFN_DPP_ROW_MIRROR>(v);
+  else if constexpr (BIT == 4) return v + dpp_mov<SFN_DPP_HALF_MIRROR>(v);
+  else if constexpr (BIT == 2) return v + dpp_mov<SFN_DPP_XOR2>(v);
+  else return v + dpp_mov<SFN_DPP_XOR1>(v);
+}
+
+template <int NV, int BIT>
+__device__ __forceinline__ void transpose_sum_rec(float* s) {
+  if constexpr (BIT > 0) {
+    if constexpr (NV > 1) {
+      halve_step<BIT, NV / 2>(s);
+      transpose_sum_rec<NV / 2, BIT / 2>(s);
+    } else {
+      s[0] = lane_pair_sum<BIT>(s[0]);
+      transpose_sum_rec<1, BIT / 2>(s);
+    }
+  }
+}
+
 // Reduce V values per lane over the 64 lanes of a wave at once (V a power of two,
-// V <= 64). On return lane l holds, in s[0], the wave total of value index
-//   vidx(l) = sum over the top log2(V) lane bits, i.e. l >> (6 - log2 V),
-// identical in all 64/V lanes that share those bits. Each halving step exchanges half
-// of the remaining values with the partner lane across one lane bit, so the work is
-// V - 1 + (6 - log2 V) exchanges instead of 6 V.
+// V <= 16). On return lane l holds, in s[0], the wave total of value index
+// l >> (6 - log2 V) (the top log2 V lane bits), identical in the 64/V lanes that share
+// those bits. Each halving step exchanges half of the remaining values with the partner
+// lane across one lane bit, so the work is V - 1 + (6 - log2 V) exchanges instead of 6 V.
+// Larger sets are reduced as independent blocks of 16.
 template <int V>
 __device__ __forceinline__ void wave_transpose_sum(float* s) {
-  const int lane = threadIdx.x & 63;
-  int nv = V;
-  int bit = 32;
-#pragma unroll
-  for (int step = 0; step < 6; ++step) {
-    if (nv > 1) {
-      const bool upper = (lane & bit) != 0;
-      const int half = nv >> 1;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i < half) {
-          const float keep = upper ? s[i + half] : s[i];
-          const float send = upper ? s[i] : s[i + half];
-          s[i] = keep + shfl_xor_f(send, bit);
-        }
-      }
-      nv = half;
-    } else {
-      if (bit >= 16) {
-        s[0] += shfl_xor_f(s[0], bit);
-      } else if (bit == 8) {
-        s[0] += dpp_mov<SFN_DPP_ROW_MIRROR>(s[0]);
-      } else if (bit == 4) {
-        s[0] += dpp_mov<SFN_DPP_HALF_MIRROR>(s[0]);
-      } else if (bit == 2) {
-        s[0] += dpp_mov<SFN_DPP_XOR2>(s[0]);
-      } else {
-        s[0] += dpp_mov<SFN_DPP_XOR1>(s[0]);
-      }
-    }
-    bit >>= 1;
-  }
+  static_assert(V <= 16, "reduce larger sets in blocks of 16");
+  transpose_sum_rec<V, 32>(s);
 }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
