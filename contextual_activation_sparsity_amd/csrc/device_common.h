@@ -60,6 +60,7 @@ struct Chunk<WT_F32> {
 };
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 // Global-address-space pointers. Pointers that arrive inside a by-value argument struct
 // are generic; accessing through them would emit flat instructions, which count against

@@ -10,24 +10,15 @@
 namespace sfn {
 
 // Workspace layout shared by every call on a workspace:
-//   [0, 256)            decode control words (Ctrl)
+//   [0, 256)            reserved
 //   [256, 1280)         dense-chunk column-tile arrival counters (256 x uint32)
 //   [1280, kWsHeader)   reserved
 //   [kWsHeader, ...)    per-call scratch, rewritten by each call before it is read
-// The header is zero-filled once by the caller; each call leaves its counters at zero
-// (the decode release word only ever increases). Scratch of one call may overlap scratch
-// of another, never the header.
+// The header is zero-filled once by the caller; each call leaves its counters at zero.
+// Scratch of one call may overlap scratch of another, never the header.
 constexpr size_t kWsHeader = 2048;
 constexpr size_t kWsChunkCounters = 256;
 constexpr int kMaxColTiles = 256;
-
-struct Ctrl {
-  uint32_t arrive;   // workgroups that finished their partial in the current launch
-  uint32_t release;  // bumped by the last arriving workgroup
-  uint32_t error;    // nonzero if a bounded wait gave up (never expected)
-  uint32_t pad[61];
-};
-static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 
 struct DecodeArgs {
   const char* wg;
@@ -42,15 +33,20 @@ struct DecodeArgs {
   float* y;                // [nb, d] or null
   int32_t* active_idx;     // [nb, f] or null
   int32_t* n_active;       // [nb] or null
-  Ctrl* ctrl;
-  int32_t* tile_cnt;  // [G, 4]
-  int32_t* tile_idx;  // [4, f]
-  float* part;        // [G, nb, d]
+  int32_t* tile_cnt;  // [G, 8]: union count, then one count per token
+  int32_t* tile_idx;  // [4, f]: per-token active rows, by tile
+  int32_t* sel_idx;   // [f]: rows active for some token, by tile
+  float* sel_a;       // [4, f]: their activations
+  uint8_t* sel_bits;  // [f]: their per-token mask bits
+  float* part;        // [G * rows side by side, nb, d]
   int d, f, nch, row_bytes, nb, act, G, n_red;
 };
 
-// Decode: workgroups for f neurons, reducing workgroups, rows a workgroup handles side
-// by side (partials per workgroup), workspace bytes, carving of the workspace.
+// Decode (three launches per call: a gate kernel over tiles of rows that writes compacted
+// active lists, an up/down kernel that splits the concatenated list evenly and writes
+// fp32 partials of y, and a reduce kernel that sums them in a fixed order):
+// workgroups per launch for f neurons, reducing workgroups, rows a workgroup handles
+// side by side (partials per workgroup), workspace bytes, carving of the workspace.
 int decode_grid(int f);
 int decode_reducers(int G, int nb, int d);
 int decode_rows_side_by_side(int nch);

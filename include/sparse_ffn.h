@@ -34,14 +34,12 @@
  *     the caller's next synchronisation. No C++ exception crosses the ABI.
  *   - Workspace: `ws` of `ws_bytes` bytes (256-byte aligned), sized by the
  *     *_workspace_size queries. Its first 2 KiB hold control words that persist between
- *     calls (the decode kernel's arrival counter, the dense chunk's column-tile
- *     counters); everything after them is scratch each call rewrites before reading.
- *     It must be zero-filled once when it is allocated (e.g. torch.zeros); every call
- *     leaves its counters at zero again when it completes, so any sequence of calls on
- *     one stream may share one workspace (sized for the largest of them). Calls that may
- *     run concurrently (different streams) need distinct workspaces. A decode launch
- *     that finds its counter not at zero writes nothing and sets a flag at byte offset
- *     8 of the workspace.
+ *     calls (the dense chunk's column-tile arrival counters); everything after them is
+ *     scratch each call rewrites before reading. It must be zero-filled once when it is
+ *     allocated (e.g. torch.zeros); every call leaves its counters at zero again when
+ *     it completes, so any sequence of calls on one stream may share one workspace
+ *     (sized for the largest of them). Calls that may run concurrently (different
+ *     streams) need distinct workspaces.
  *   - Outputs are deterministic: identical inputs give bitwise identical y, index
  *     lists and thresholds (fixed reduction orders, no floating-point atomics).
  *   - Arithmetic: products and sums in fp32 (bf16 inputs are widened exactly).
