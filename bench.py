@@ -7,19 +7,28 @@ seeds, batch 1, every layer of every token fed its own x ~ N(0, I) (bf16). CATS
 thresholds are calibrated per layer by the library (256 calibration tokens) for the
 headline sparsity (50%) and for the sweep points (70/80/90%).
 
-A step is one decode token through all 32 layers (32 sparse_ffn_decode calls, one fused
-kernel each). After W untimed warm-up steps, K steps are timed with HIP events on the
-stream the kernels run on. The JSON line on stdout carries:
+A step is one decode token through all 32 layers (32 sparse_ffn_decode calls; each call
+is three kernels: gate, up/down, reduce). After W untimed warm-up steps, K steps are
+timed with HIP events on the stream the kernels run on (graph mode: one captured graph
+per token, replayed back to back). The JSON line on stdout carries:
   value      decode tokens/s at the headline sparsity (inputs resident in HBM)
-  roofline   the decode kernel's algorithmic bytes per launch (gate rows, the active
-             up and down rows, x and y) over its average launch duration, measured with
-             events around each launch, against the 8 TB/s HBM peak; `traffic` comes from
-             the committed rocprofv3 counter summary when it matches the kernel source
+  roofline   one sparse_ffn_decode call: algorithmic bytes per call (all gate rows, the
+             active up and down rows, x and y) over the average call duration in the
+             timed region, against the 8 TB/s HBM peak; `stages` splits the call into
+             the gate kernel (timed alone, from calls that request no output) and the
+             rest; `traffic` is the HBM bytes per call from the committed rocprofv3
+             counter summary, when that summary was taken on the current kernel source
   cpu_baseline  the CPU oracle (dense FFN then mask, numpy float64) timed on a bounded
              sample of layers and tokens of the same workload on this host
   dense_path the same stack through the library's dense path (ffn_dense_chunk, n = 1)
   sweep      tokens/s, density and GB/s at the other sparsities
 Progress goes to stderr.
+
+Profiling helpers (no GPU needed): --summarize-trace DIR turns a rocprofv3
+--kernel-trace --stats CSV output into a markdown table; --summarize-traffic FETCH_DIR
+WRITE_DIR turns two --pmc CSV outputs (FETCH_SIZE, then WRITE_SIZE) of a
+`--copy-probe` run into HBM bytes per decode call, scaled by what the counters read for
+the probe's plain copy of known size.
 """
 
 import argparse
@@ -61,7 +70,74 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="before the stack, copy a MIB-MiB buffer three times (counter scaling)")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--command", default="", help="profiling command recorded in a summary")
     return ap.parse_args()
+
+
+DECODE_KERNELS = ("decode_gate_kernel", "decode_updown_kernel", "decode_reduce_kernel")
+COPY_KERNEL = "copy_kernel"
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for fn in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(fn, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return rows
+
+
+def _short(name):
+    for k in DECODE_KERNELS + ("chunk_stage1_kernel", "chunk_stage2_kernel", "score_kernel", "hist_kernel",
+                               "pick_kernel", "svd_z_kernel", "svd_p_kernel"):
+        if k in name:
+            return k
+    if "elementwise_kernel" in name and "neg" in name.lower():
+        return COPY_KERNEL
+    return name[:60]
+
+
+def summarize_trace(d, command):
+    rows = _csv_rows(d, "kernel_stats.csv")
+    out = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", command or "(not recorded)", "```", "",
+           "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    avg = {_short(r["Name"]): float(r["AverageNs"]) / 1e3 for r in rows}
+    if all(k in avg for k in DECODE_KERNELS):
+        out += ["", "One sparse_ffn_decode call is one dispatch of each decode kernel: "
+                f"{' + '.join(f'{avg[k]:.2f}' for k in DECODE_KERNELS)} = "
+                f"{sum(avg[k] for k in DECODE_KERNELS):.2f} us of kernel time per call. "
+                "bench.py also times calls that request no output, which run the gate kernel alone, "
+                "so that kernel has more dispatches than the other two."]
+    print("\n".join(out))
+
+
+def summarize_traffic(fetch_dir, write_dir, probe_bytes):
+    """Median FETCH_SIZE / WRITE_SIZE bytes per dispatch of each kernel (the counters are
+    in KiB), and what they read for the probe's copy of probe_bytes bytes."""
+    import statistics
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r.get("Counter_Name") != counter:
+                continue
+            per.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]) * 1024.0)
+        copies = per.get(COPY_KERNEL)
+        if not copies:
+            raise SystemExit(f"{counter}: the copy probe's kernel is missing")
+        res[counter] = {"per_kernel_bytes": {k: statistics.median(v) for k, v in per.items()},
+                        "copy_probe_bytes_counted": statistics.median(copies), "copy_probe_bytes": probe_bytes}
+    return res
 
 
 class Stack:
@@ -152,25 +228,6 @@ def time_steps(torch, fn, step_args, mode):
     return e0.elapsed_time(e1)
 
 
-def kernel_durations(torch, fn, step_args):
-    """Per-launch durations (ms) from events recorded on the launch stream right before
-    and after each call (one kernel per call)."""
-    stream = torch.cuda.current_stream()
-    evs = []
-    torch.cuda.synchronize()
-    for calls in step_args:
-        for a in calls:
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record(stream)
-            st = fn(*a)
-            e.record(stream)
-            if st != 0:
-                raise RuntimeError(f"library call failed with status {st}")
-            evs.append((s, e))
-    torch.cuda.synchronize()
-    return [s.elapsed_time(e) for s, e in evs]
-
-
 def cpu_baseline(stack, k, budget_s):
     """The oracle as it stands, timed on this host on a bounded sample: whole layers,
     weights widened to float64 beforehand (not timed), tokens one at a time."""
@@ -219,6 +276,11 @@ def cpu_baseline(stack, k, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.command)
+        return 0
+    if args.summarize_traffic:
+        return write_traffic(args.summarize_traffic, args.copy_probe << 20, args.command)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Run with --gpus 1.", file=sys.stderr)
@@ -228,6 +290,16 @@ def main():
     from contextual_activation_sparsity_amd import binding as B
     from contextual_activation_sparsity_amd import inputs
 
+    if args.copy_probe:
+        # a plain elementwise kernel of known traffic: reads n bytes, writes n bytes
+        n = args.copy_probe << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy probe: 3 elementwise copies of {n} bytes")
+        del src, dst
     K, W = args.steps, args.warmup
     sweep = [float(s) for s in args.sweep.split(",") if s.strip()] if args.sweep else []
     n_tok = K + W
@@ -260,25 +332,34 @@ def main():
     tok_s = 1e3 / ms_step
     log(f"  {ms_step:.3f} ms/step, {tok_s:.1f} tokens/s, density {nact.mean() / f:.4f}")
 
-    # roofline of the decode kernel: events around each launch of the timed tokens
-    durs = kernel_durations(torch, lib.sparse_ffn_decode, [stack.decode_args(tok, args.sparsity, stream)
-                                                            for tok in steps_tok])
-    durs = np.array(durs)
-    per_launch_bytes = 2.0 * f * d + 6.0 * d + 4.0 * d * nact.mean()
-    avg_ms = float(durs.mean())
-    achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
+    # roofline of one decode call: the timed region above, per call
+    call_us = ms_step * 1e3 / L
+    per_call_bytes = 2.0 * f * d + 6.0 * d + 4.0 * d * nact.mean()
+    achieved = per_call_bytes / (call_us * 1e-6) / 1e9
+    # the gate kernel alone: calls that request no output launch only the gate kernel
+    gate_steps = [[a[:7] + (None, None, None) + a[10:] for a in stack.decode_args(tok, args.sparsity, stream)]
+                  for tok in steps_tok]
+    time_steps(torch, lib.sparse_ffn_decode, gate_steps[:W], args.mode)
+    gate_us = time_steps(torch, lib.sparse_ffn_decode, gate_steps, args.mode) * 1e3 / (K * L)
+    gate_bytes = 2.0 * f * d + 2.0 * d
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
             tr = json.load(fh)
         if tr.get("kernel_hash") == kernel_hash():
-            traffic = tr.get("bytes_per_launch")
+            traffic = tr.get("bytes_per_call")
     roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                "kernel": "decode_kernel (bf16, batch 1, d 4096)",
-                "algorithmic_bytes_per_launch": per_launch_bytes, "avg_launch_us": avg_ms * 1e3,
-                "launches": int(durs.size)}
-    log(f"  decode kernel: {avg_ms * 1e3:.2f} us/launch, {achieved:.1f} GB/s algorithmic ({achieved / PEAK_HBM_GBS:.3f})")
+                "kernel": "sparse_ffn_decode call (decode_gate_kernel + decode_updown_kernel + decode_reduce_kernel), "
+                          "bf16, batch 1, d 4096, f 11008",
+                "algorithmic_bytes_per_launch": per_call_bytes, "avg_launch_us": call_us, "launches": K * L,
+                "stages": {"gate_kernel": {"us": gate_us, "bytes": gate_bytes,
+                                           "gbs": gate_bytes / (gate_us * 1e-6) / 1e9},
+                           "updown_and_reduce_kernels": {"us": call_us - gate_us, "bytes": per_call_bytes - gate_bytes,
+                                                         "gbs": (per_call_bytes - gate_bytes)
+                                                         / ((call_us - gate_us) * 1e-6) / 1e9}}}
+    log(f"  decode call: {call_us:.2f} us, {achieved:.1f} GB/s algorithmic ({achieved / PEAK_HBM_GBS:.3f}); "
+        f"gate kernel alone {gate_us:.2f} us")
 
     result_sweep = []
     for k in sweep:
@@ -319,6 +400,31 @@ def main():
         "sweep": result_sweep,
     }
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def write_traffic(dirs, probe, command):
+    """HBM bytes per decode call: FETCH_SIZE and WRITE_SIZE of the three decode kernels,
+    each counter scaled so that the probe's copy of `probe` bytes reads (writes) exactly
+    `probe` bytes."""
+    if probe <= 0:
+        raise SystemExit("--copy-probe MIB must give the probe's size")
+    res = summarize_traffic(dirs[0], dirs[1], probe)
+    per_call = 0.0
+    detail = {}
+    for counter, r in res.items():
+        scale = probe / r["copy_probe_bytes_counted"]
+        ks = {k: v * scale for k, v in r["per_kernel_bytes"].items() if k in DECODE_KERNELS}
+        detail[counter] = {"scale": scale, "probe_counted_bytes": r["copy_probe_bytes_counted"],
+                           "per_kernel_bytes": ks}
+        per_call += sum(ks.values())
+    out = {"kernel_hash": kernel_hash(), "bytes_per_call": per_call, "counters": detail, "command": command,
+           "note": "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median over dispatches) of the three decode "
+                   "kernels, summed; each counter scaled by probe bytes / what it reads for a plain elementwise "
+                   "copy (torch.neg) of 1 GiB in the same run. kernel_hash covers the decode kernel sources."}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
     return 0
 
 
