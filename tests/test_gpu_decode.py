@@ -27,8 +27,9 @@ def _tol(dtype):
     return TOL_BF16 if dtype == "bf16" else TOL_F32
 
 
-def _ctrl_error(ws):
-    return int(ws[8:12].view(torch.int32).item())
+def _header_clear(ws):
+    """The first 2 KiB of a workspace hold counters that every call leaves at zero."""
+    return not bool(ws[:2048].any().item())
 
 
 def run_decode(layer, x_dev, t_val, ws, mask=None, want_y=True, cand=None, n_cand=None):
@@ -41,7 +42,7 @@ def run_decode(layer, x_dev, t_val, ws, mask=None, want_y=True, cand=None, n_can
     B.sparse_ffn_decode(layer, x_dev, t, ws, y=y, mask_in=m, active_idx=idx, n_active=n_act, cand=cand,
                         n_cand=n_cand)
     torch.cuda.synchronize()
-    assert _ctrl_error(ws) == 0
+    assert _header_clear(ws)
     return (y.cpu().numpy() if want_y else None), idx.cpu().numpy(), n_act.cpu().numpy()
 
 
@@ -217,7 +218,7 @@ def test_candidate_mode_reglu():
 def test_one_workspace_shared_by_every_call():
     """calibrate -> decode -> dense chunk -> predictor -> decode -> calibrate -> decode on a
     single workspace: each call must leave the persistent control words as it found them
-    (regression: the calibration state used to overlap the decode arrival counter)."""
+    (regression: the calibration state once overlapped a decode counter)."""
     w = inputs.workload(1)
     d, f, n_cal = 2048, 3000, 64
     raw, dev, host = swiglu_layer_dev(w, 0, d=d, f=f)
@@ -238,7 +239,7 @@ def test_one_workspace_shared_by_every_call():
         n_act = torch.empty(1, dtype=torch.int32, device="cuda")
         B.sparse_ffn_decode(layer, to_dev(xs_raw[j:j + 1], "bf16"), t_dev, ws, y=y, active_idx=idx, n_active=n_act)
         torch.cuda.synchronize()
-        assert _ctrl_error(ws) == 0
+        assert _header_clear(ws)
         t = float(t_dev.item())
         gm = mask_from_idx(idx.cpu().numpy()[0], int(n_act.item()), f)
         om, oa, _ = oracle.cats_decode(Wg, Wu, Dt, xs[j][None], t)
