@@ -124,21 +124,28 @@ struct Shape {
       }
   }
 
-  // Wave totals of NV values per thread into wpart[wave][0..NV): blocks of up to 16 values
-  // are transposed and summed across the wave, then written by one lane each.
-  template <int NV>
-  __device__ __forceinline__ static void reduce_to_lds(float (*wpart)[NV], float (&s)[NV]) {
-    constexpr int BLK = NV < 16 ? NV : 16;
+  // Wave totals of NV values per thread into wpart[wave][0..NV): the values are cut into
+  // power-of-two blocks of at most 16 (e.g. 24 = 16 + 8), each transposed and summed
+  // across the wave, then written by one lane per value.
+  template <int NV, int OFF, int BLK>
+  __device__ __forceinline__ static void reduce_block(float (*wpart)[NV], const float (&s)[NV]) {
     constexpr int LOGB = (BLK >= 16) ? 4 : (BLK >= 8) ? 3 : (BLK >= 4) ? 2 : (BLK >= 2) ? 1 : 0;
     constexpr int SH = 6 - LOGB;
     const int lane = threadIdx.x & 63;
+    float t[BLK];
 #pragma unroll
-    for (int blk = 0; blk < NV / BLK; ++blk) {
-      float t[BLK];
-#pragma unroll
-      for (int i = 0; i < BLK; ++i) t[i] = s[blk * BLK + i];
-      wave_transpose_sum<BLK>(t);
-      if ((lane & ((1 << SH) - 1)) == 0) wpart[threadIdx.x >> 6][blk * BLK + (lane >> SH)] = t[0];
+    for (int i = 0; i < BLK; ++i) t[i] = s[OFF + i];
+    wave_transpose_sum<BLK>(t);
+    if ((lane & ((1 << SH) - 1)) == 0) wpart[threadIdx.x >> 6][OFF + (lane >> SH)] = t[0];
+  }
+
+  template <int NV, int OFF = 0>
+  __device__ __forceinline__ static void reduce_to_lds(float (*wpart)[NV], const float (&s)[NV]) {
+    constexpr int REM = NV - OFF;
+    if constexpr (REM > 0) {
+      constexpr int BLK = REM >= 16 ? 16 : REM >= 8 ? 8 : REM >= 4 ? 4 : REM >= 2 ? 2 : 1;
+      reduce_block<NV, OFF, BLK>(wpart, s);
+      reduce_to_lds<NV, OFF + BLK>(wpart, s);
     }
   }
 
@@ -525,13 +532,17 @@ struct UpDownKernel {
 };
 
 // ---------------------------------------------------------------------- reduce kernel
-// y = sum of the partials of the up/down kernel, column slice by column slice, in a
-// fixed order (deterministic). Workgroup 0 also assembles the per-token active lists.
-template <int RPG>
+// y = sum of the partials of the up/down kernel, in chunks of 32 columns (128 bytes of
+// each partial row): lane l of group g sums column l of partials g, g + 16, g + 32, ...
+// (16 loads in flight), then group 0 adds the 16 group sums in order, so y is
+// deterministic. Workgroup 0 also assembles the per-token active index lists.
+constexpr int kRedCols = 32;
+constexpr int kRedGroups = 16;
+
 struct ReduceKernel {
-  static constexpr int kRT = 256;  // threads
+  static constexpr int kRT = kRedCols * kRedGroups;  // 512 threads
   struct Smem {
-    float red[kRT];
+    float red[kRedGroups][kRedCols];
     int pref[kGMax + 1];
     int wsum[kRT / 64];
   };
@@ -566,7 +577,7 @@ struct ReduceKernel {
     __syncthreads();
   }
 
-  __device__ static void run(const DecodeArgs& args) {
+  __device__ static void run(const DecodeArgs& args, int P) {
     const DevArgs a = dev_args(args);
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -574,40 +585,32 @@ struct ReduceKernel {
     const int nb = a.nb;
     if (a.y) {
       const int L = nb * a.d;
-      const int P = a.G * RPG;
-      const int s0 = share_begin(ri, L, a.n_red);
-      const int SL = share_begin(ri + 1, L, a.n_red) - s0;
-      const int slmax = (L + a.n_red - 1) / a.n_red;
-      if (slmax <= kRT) {
-        const int npg = kRT / slmax;
-        const int e = tid % slmax, pg = tid / slmax;
+      const int nck = (L + kRedCols - 1) / kRedCols;
+      const int c0 = share_begin(ri, nck, a.n_red), c1 = share_begin(ri + 1, nck, a.n_red);
+      const int col = tid % kRedCols, g = tid / kRedCols;
+      for (int ck = c0; ck < c1; ++ck) {
+        const int e = ck * kRedCols + col;
+        const bool ok = e < L;
+        const SFN_GLOBAL float* src = a.part + (ok ? e : 0);
         float sum = 0.f;
-        if (pg < npg && e < SL) {
-          const SFN_GLOBAL float* src = a.part + s0 + e;
-          int p = pg;
-          // eight loads in flight, summed in partial order
-          for (; p + 7 * npg < P; p += 8 * npg) {
-            float v[8];
+        int p = g;
+        for (; p + (kRedGroups - 1) * kRedGroups < P; p += kRedGroups * kRedGroups) {
+          float v[kRedGroups];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(p + u * npg) * L];
+          for (int u = 0; u < kRedGroups; ++u) v[u] = src[(size_t)(p + u * kRedGroups) * L];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) sum += v[u];
-          }
-          for (; p < P; p += npg) sum += src[(size_t)p * L];
+          for (int u = 0; u < kRedGroups; ++u) sum += v[u];
         }
-        sm.red[tid] = sum;
+        for (; p < P; p += kRedGroups) sum += src[(size_t)p * L];
+        sm.red[g][col] = sum;
         __syncthreads();
-        if (pg == 0 && e < SL) {
-          float tot = sm.red[e];
-          for (int g2 = 1; g2 < npg; ++g2) tot += sm.red[g2 * slmax + e];
-          a.y[s0 + e] = tot;
+        if (g == 0 && ok) {
+          float tot = sm.red[0][col];
+#pragma unroll
+          for (int j = 1; j < kRedGroups; ++j) tot += sm.red[j][col];
+          a.y[e] = tot;
         }
-      } else {
-        for (int e = tid; e < SL; e += kRT) {
-          float sum = 0.f;
-          for (int p = 0; p < P; ++p) sum += a.part[(size_t)p * L + s0 + e];
-          a.y[s0 + e] = sum;
-        }
+        __syncthreads();
       }
     }
     const bool want_idx = a.active_idx != nullptr || a.n_active != nullptr;
@@ -641,18 +644,17 @@ __global__ __launch_bounds__(kNT) void decode_updown_kernel(DecodeArgs a) {
   UpDownKernel<WT, BMAX, CPT, TPR, R>::run(a);
 }
 
-template <int RPG>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
-  ReduceKernel<RPG>::run(a);
-}
+__global__ __launch_bounds__(512) void decode_reduce_kernel(DecodeArgs a, int P) { ReduceKernel::run(a, P); }
 
-template <int WT, int BMAX, int CPT, int TPR, int R>
+// RGATE / RUP: rows each thread holds per half step of the gate / per up-down step.
+template <int WT, int BMAX, int CPT, int TPR, int RGATE, int RUP>
 hipError_t launch_pair(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.G), block(kNT);
-  hipLaunchKernelGGL((decode_gate_kernel<WT, BMAX, CPT, TPR, R>), grid, block, 0, s, a);
-  if (a.y) hipLaunchKernelGGL((decode_updown_kernel<WT, BMAX, CPT, TPR, R>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((decode_gate_kernel<WT, BMAX, CPT, TPR, RGATE>), grid, block, 0, s, a);
+  if (a.y) hipLaunchKernelGGL((decode_updown_kernel<WT, BMAX, CPT, TPR, RUP>), grid, block, 0, s, a);
   if (a.y || a.active_idx || a.n_active)
-    hipLaunchKernelGGL((decode_reduce_kernel<kNT / TPR>), dim3(a.y ? a.n_red : 1), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.y ? a.n_red : 1), dim3(ReduceKernel::kRT), 0, s, a,
+                       a.G * (kNT / TPR));
   return hipGetLastError();
 }
 
@@ -661,13 +663,14 @@ hipError_t dispatch_tpr(const DecodeArgs& a, hipStream_t s) {
   // rows per thread per half step: 16 weight loads in flight per thread and buffer for
   // one token, 8 for four tokens (the dot-product registers grow with the batch)
   constexpr int RB = BMAX == 1 ? 8 : 4;
+  constexpr int RG1 = RB;
   if (a.nch > 2048) return hipErrorInvalidValue;
-  if (a.nch > 1024) return launch_pair<WT, BMAX, 4, 512, RB / 4>(a, s);
-  if (a.nch > 512) return launch_pair<WT, BMAX, 2, 512, RB / 2>(a, s);
-  if (a.nch > 256) return launch_pair<WT, BMAX, 1, 512, RB>(a, s);
-  if (a.nch > 128) return launch_pair<WT, BMAX, 1, 256, RB>(a, s);
-  if (a.nch > 64) return launch_pair<WT, BMAX, 1, 128, RB>(a, s);
-  return launch_pair<WT, BMAX, 1, 64, 4>(a, s);
+  if (a.nch > 1024) return launch_pair<WT, BMAX, 4, 512, RB / 4, RB / 4>(a, s);
+  if (a.nch > 512) return launch_pair<WT, BMAX, 2, 512, RB / 2, RB / 2>(a, s);
+  if (a.nch > 256) return launch_pair<WT, BMAX, 1, 512, RG1, RB>(a, s);
+  if (a.nch > 128) return launch_pair<WT, BMAX, 1, 256, RB, RB>(a, s);
+  if (a.nch > 64) return launch_pair<WT, BMAX, 1, 128, RB, RB>(a, s);
+  return launch_pair<WT, BMAX, 1, 64, 4, 4>(a, s);
 }
 
 }  // namespace
@@ -689,7 +692,7 @@ int decode_grid(int f) {
 
 int decode_reducers(int G, int nb, int d) {
   (void)G;
-  int n = (nb * d + 15) / 16;  // 16 columns per reducing workgroup
+  int n = (nb * d + kRedCols - 1) / kRedCols;  // one 32-column chunk per reducing workgroup
   if (n > kGMax) n = kGMax;
   return n < 1 ? 1 : n;
 }
