@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other workloads (batch 4, SVD pipeline, 70B-shape decode and 16-token chunk)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before the stack, copy a MIB-MiB buffer three times (counter scaling)")
     ap.add_argument("--summarize-trace", metavar="DIR")
@@ -228,6 +230,213 @@ def time_steps(torch, fn, step_args, mode):
     return e0.elapsed_time(e1)
 
 
+def time_mixed(torch, steps, mode):
+    """Like time_steps, for steps whose calls go to different library functions:
+    steps = [[(fn, args_without_stream), ...], ...]. Returns ms for all steps."""
+    stream = torch.cuda.current_stream()
+
+    def run(step, st):
+        for fn, a in step:
+            rc = fn(*a, st)
+            if rc != 0:
+                raise RuntimeError(f"library call failed with status {rc}")
+
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if mode == "graph":
+        graphs = []
+        cap = torch.cuda.Stream()
+        for step in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                run(step, cap.cuda_stream)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for g in graphs:
+            g.replay()
+        e1.record(stream)
+    else:
+        e0.record(stream)
+        for step in steps:
+            run(step, stream.cuda_stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4):
+    """The other workloads, each timed like the headline (graphs of per-layer calls, HIP
+    events over the timed steps) on n_layers independently seeded layers: per-call time,
+    algorithmic bytes and GB/s. Inputs as in the headline: on-device Gaussian weights,
+    x ~ N(0, I) in bf16, thresholds from the library's own calibration."""
+    import numpy as np
+    lib = B.raw()
+    dev = "cuda"
+    out = {}
+
+    def gauss(shape, std, seed):
+        return inputs.torch_gaussian_bf16(shape, std, seed, dev)
+
+    def xtok(w, shape, stream_id):
+        g = torch.Generator(device=dev)
+        g.manual_seed(1_000_000 * w.index + stream_id)
+        return torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+
+    def swiglu_layers(w, d, f, nl):
+        return [B.FFNLayer(gauss((f, d), w.w_std, inputs.seed(w.index, l, inputs.T_GATE)),
+                           gauss((f, d), w.w_std, inputs.seed(w.index, l, inputs.T_UP)),
+                           gauss((f, d), w.w_std, inputs.seed(w.index, l, inputs.T_DOWN))) for l in range(nl)]
+
+    def calibrate(layers, w, k, ws):
+        xc = torch.from_numpy(inputs.tokens(w, w.n_cal, inputs.STREAM_CAL, d=layers[0].d).view(np.int16))
+        xc = xc.view(torch.bfloat16).to(dev)
+        t = torch.zeros(len(layers), dtype=torch.float32, device=dev)
+        for l, layer in enumerate(layers):
+            B.sparse_ffn_calibrate(layer, xc, k, t[l:l + 1], ws)
+        return t
+
+    def decode_leg(name, w, d, f, batch, k, nl):
+        layers = swiglu_layers(w, d, f, nl)
+        ws = B.workspace(max(B.sparse_ffn_workspace_size(layers[0], max(batch, w.n_cal)),
+                             B.sparse_ffn_workspace_size(layers[0], 16)))
+        t = calibrate(layers, w, k, ws)
+        X = xtok(w, (n_warm + n_steps, nl, batch, d), inputs.STREAM_DECODE)
+        y = torch.zeros((nl, batch, d), dtype=torch.float32, device=dev)
+        idx = torch.zeros((batch, f), dtype=torch.int32, device=dev)
+        nact = torch.zeros(batch, dtype=torch.int32, device=dev)
+        wsp, wsb = ws.data_ptr(), ws.numel()
+
+        def call(tok, l, counts=False):
+            return (lib.sparse_ffn_decode, (ctypes.byref(layers[l].c), X[tok, l].data_ptr(), batch,
+                                            t[l:l + 1].data_ptr(), None, None, None, y[l].data_ptr(),
+                                            idx.data_ptr() if counts else None,
+                                            nact.data_ptr() if counts else None, wsp, wsb))
+        # union density from the index lists of an untimed pass over the timed tokens
+        union = []
+        for tok in range(n_warm, n_warm + n_steps):
+            for l in range(nl):
+                fn, a = call(tok, l, True)
+                fn(*a, torch.cuda.current_stream().cuda_stream)
+                torch.cuda.synchronize()
+                m = torch.zeros(f, dtype=torch.bool, device=dev)
+                for b in range(batch):
+                    m[idx[b, :int(nact[b].item())].long()] = True
+                union.append(int(m.sum().item()))
+        u = float(np.mean(union))
+        time_mixed(torch, [[call(tok, l) for l in range(nl)] for tok in range(n_warm)], mode)
+        ms = time_mixed(torch, [[call(tok, l) for l in range(nl)] for tok in range(n_warm, n_warm + n_steps)], mode)
+        us = ms * 1e3 / (n_steps * nl)
+        byts = 2.0 * f * d + 4.0 * d * u + 2.0 * batch * d + 4.0 * batch * d
+        out[name] = {"d": d, "f": f, "batch": batch, "sparsity": k, "layers_timed": nl, "us_per_call": us,
+                     "union_density": u / f, "algorithmic_bytes_per_call": byts,
+                     "gbs": byts / (us * 1e-6) / 1e9, "tokens_per_s_32_layers": batch / (32 * us * 1e-6)}
+        log(f"  extra {name}: {us:.2f} us/call, union density {u / f:.4f}, {out[name]['gbs']:.0f} GB/s")
+        del layers, ws, X, y
+        torch.cuda.empty_cache()
+
+    # batch of 4 with per-token masks and the union gather (Llama-3-8B shape), and batch 1
+    w2 = inputs.workload(2)
+    decode_leg("llama3_8b_b4_k50", w2, w2.d, w2.f, 4, 0.5, n_layers)
+    decode_leg("llama3_8b_b1_k50", w2, w2.d, w2.f, 1, 0.5, n_layers)
+    # sparse decode at the Llama-3-70B shape (d 8192: two 16-byte chunks per thread)
+    w4 = inputs.workload(4)
+    decode_leg("llama3_70b_b1_k50", w4, w4.d, w4.f, 1, 0.5, 2)
+
+    # 16-token dense verification chunk at the Llama-3-70B shape
+    layers = swiglu_layers(w4, w4.d, w4.f, 2)
+    ws = B.workspace(B.sparse_ffn_workspace_size(layers[0], 16))
+    X = xtok(w4, (n_warm + n_steps, 2, 16, w4.d), inputs.STREAM_DECODE)
+    Y = torch.zeros((2, 16, w4.d), dtype=torch.float32, device=dev)
+    wsp, wsb = ws.data_ptr(), ws.numel()
+
+    def chunk(tok, l):
+        return (lib.ffn_dense_chunk, (ctypes.byref(layers[l].c), X[tok, l].data_ptr(), 16, Y[l].data_ptr(), wsp, wsb))
+    time_mixed(torch, [[chunk(tok, l) for l in range(2)] for tok in range(n_warm)], mode)
+    ms = time_mixed(torch, [[chunk(tok, l) for l in range(2)] for tok in range(n_warm, n_warm + n_steps)], mode)
+    us = ms * 1e3 / (n_steps * 2)
+    byts = 6.0 * w4.f * w4.d + 2.0 * 16 * w4.d + 4.0 * 16 * w4.d
+    out["llama3_70b_chunk16"] = {"d": w4.d, "f": w4.f, "tokens": 16, "us_per_call": us,
+                                 "algorithmic_bytes_per_call": byts, "gbs": byts / (us * 1e-6) / 1e9,
+                                 "tflops": 2.0 * 3 * w4.f * w4.d * 16 / (us * 1e-6) / 1e12,
+                                 "ms_per_chunk_8_layers": 8 * us / 1e3}
+    log(f"  extra chunk16: {us:.1f} us/layer, {out['llama3_70b_chunk16']['gbs']:.0f} GB/s")
+    del layers, ws, X, Y
+    torch.cuda.empty_cache()
+
+    # ReGLU layers with the rank-256 SVD predictor, sequential pipeline (predict, then the
+    # gate on the candidates and up/down where ReLU(gate) > 0)
+    w3 = inputs.workload(3)
+    d, f, r = w3.d, w3.f, w3.rank
+    preds, layers = [], []
+    xcal = xtok(w3, (w3.n_tau_cal, d), inputs.STREAM_TAU).float()
+    for l in range(n_layers):
+        A = torch.randn((f, r), generator=torch.Generator(device=dev).manual_seed(inputs.seed(3, l, inputs.T_A)),
+                        device=dev) / np.sqrt(r)
+        Bm = torch.randn((r, d), generator=torch.Generator(device=dev).manual_seed(inputs.seed(3, l, inputs.T_B)),
+                         device=dev) * w3.w_std
+        noise = torch.randn((f, d), generator=torch.Generator(device=dev).manual_seed(
+            inputs.seed(3, l, inputs.T_NOISE)), device=dev) * w3.w_std
+        wg = (A @ Bm + 0.1 * noise).to(torch.bfloat16)
+        bias = (-1.2815516 * wg.float().norm(dim=1)).contiguous()
+        # exact rank-r factors of A B: B^T = Qb Rb, so A B = (A Rb^T) Qb^T
+        Qb, Rb = torch.linalg.qr(Bm.t())
+        q = Qb.t().contiguous().to(torch.bfloat16)
+        lf = (A @ Rb.t()).contiguous().to(torch.bfloat16)
+        # per-neuron thresholds at s: between the mean prediction over calibration tokens
+        # whose gate is inactive and over those where it is active
+        P = (xcal @ q.float().t()) @ lf.float().t() + bias
+        Gt = xcal.bfloat16().float() @ wg.float().t() + bias
+        on = (Gt > 0).float()
+        n_on, n_off = on.sum(0), (1 - on).sum(0)
+        m_on = (P * on).sum(0) / n_on.clamp(min=1)
+        m_off = (P * (1 - on)).sum(0) / n_off.clamp(min=1)
+        tau = ((1 - w3.s) * m_off + w3.s * m_on)
+        tau = torch.where((n_on > 0) & (n_off > 0), tau, torch.zeros_like(tau)).contiguous()
+        del P, Gt, on, A, Bm, noise
+        layers.append(B.FFNLayer(wg, gauss((f, d), w3.w_std, inputs.seed(3, l, inputs.T_UP)),
+                                 gauss((f, d), w3.w_std, inputs.seed(3, l, inputs.T_DOWN)), b_gate=bias,
+                                 act=B.SFN_ACT_RELU))
+        preds.append(B.SVDPredictor(q, lf, tau, b=bias))
+    ws = B.workspace(max(B.sparse_ffn_workspace_size(layers[0], 1), B.svd_predict_workspace_size(preds[0])))
+    wsp_ = B.workspace(B.svd_predict_workspace_size(preds[0]))
+    X = xtok(w3, (n_warm + n_steps, n_layers, d), inputs.STREAM_DECODE)
+    y = torch.zeros((n_layers, d), dtype=torch.float32, device=dev)
+    cand = torch.zeros((n_layers, f), dtype=torch.int32, device=dev)
+    ncand = torch.zeros((n_layers, 1), dtype=torch.int32, device=dev)
+    nact = torch.zeros((n_layers, 1), dtype=torch.int32, device=dev)
+
+    def svd_calls(tok, l, counts=False):
+        return [(lib.svd_predict, (ctypes.byref(preds[l].c), X[tok, l].data_ptr(), cand[l].data_ptr(),
+                                   ncand[l].data_ptr(), None, wsp_.data_ptr(), wsp_.numel())),
+                (lib.sparse_ffn_decode, (ctypes.byref(layers[l].c), X[tok, l].data_ptr(), 1, None,
+                                         cand[l].data_ptr(), ncand[l].data_ptr(), None, y[l].data_ptr(), None,
+                                         nact[l].data_ptr() if counts else None, ws.data_ptr(), ws.numel()))]
+    dc, da = [], []
+    for tok in range(n_warm, n_warm + n_steps):
+        for l in range(n_layers):
+            for fn, a in svd_calls(tok, l, True):
+                fn(*a, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        dc.append(ncand.float().mean().item())
+        da.append(nact.float().mean().item())
+    nc, na = float(np.mean(dc)), float(np.mean(da))
+    time_mixed(torch, [[c for l in range(n_layers) for c in svd_calls(tok, l)] for tok in range(n_warm)], mode)
+    ms = time_mixed(torch, [[c for l in range(n_layers) for c in svd_calls(tok, l)]
+                            for tok in range(n_warm, n_warm + n_steps)], mode)
+    us = ms * 1e3 / (n_steps * n_layers)
+    pred_only = time_mixed(torch, [[svd_calls(tok, l)[0] for l in range(n_layers)]
+                                   for tok in range(n_warm, n_warm + n_steps)], mode) * 1e3 / (n_steps * n_layers)
+    byts = 2.0 * r * (d + f) + 8.0 * f + 2.0 * nc * d + 4.0 * na * d + 6.0 * d
+    out["reglu_svd_r256_s50"] = {"d": d, "f": f, "r": r, "s": w3.s, "layers_timed": n_layers,
+                                 "us_per_layer": us, "predictor_us": pred_only,
+                                 "candidate_density": nc / f, "active_density": na / f,
+                                 "algorithmic_bytes_per_layer": byts, "gbs": byts / (us * 1e-6) / 1e9,
+                                 "tokens_per_s_32_layers": 1.0 / (32 * us * 1e-6)}
+    log(f"  extra svd: {us:.2f} us/layer (predictor {pred_only:.2f}), cand {nc / f:.3f}, active {na / f:.3f}")
+    return out
+
+
 def cpu_baseline(stack, k, budget_s):
     """The oracle as it stands, timed on this host on a bounded sample: whole layers,
     weights widened to float64 beforehand (not timed), tokens one at a time."""
@@ -381,6 +590,11 @@ def main():
                  "speedup_of_sparse": tok_s / (1e3 / ms_d)}
         log(f"  dense path: {1e3 / ms_d:.1f} tokens/s, sparse speedup {dense['speedup_of_sparse']:.3f}")
 
+    extra = None
+    if not args.no_extras:
+        log("timing the other workloads")
+        extra = extras(B, inputs, torch, args.mode)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -398,6 +612,7 @@ def main():
         "cpu_baseline": cpu,
         "dense_path": dense,
         "sweep": result_sweep,
+        "extras": extra,
     }
     print(json.dumps(line), flush=True)
     return 0

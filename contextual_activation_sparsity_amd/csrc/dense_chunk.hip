@@ -164,28 +164,33 @@ __global__ __launch_bounds__(256) void chunk_stage2_kernel(const uint16_t* __res
     }
     return;
   }
+  // Partials cross workgroups (and XCDs, whose L2s are not coherent with each other):
+  // they are written through to memory with relaxed device-scope stores and read back
+  // the same way, and the arrival ticket is a relaxed device-scope atomic. Nothing here
+  // needs a fence, which at device scope would write back the whole L2.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = 4 * q + i;
-    if (m < n && ycol < d) part[((size_t)s * n + m) * d + ycol] = acc[i];
+    if (m < n && ycol < d)
+      __hip_atomic_store(&part[((size_t)s * n + m) * d + ycol], acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial is in memory
   __syncthreads();
   if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(&arrive[ct], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(&arrive[ct], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (old == (uint32_t)(S - 1)) ? 1u : 0u;
     if (s_last) __hip_atomic_store(&arrive[ct], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // old >= S means the counter was not zero at launch; no tile is then summed
   }
   __syncthreads();
   if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   // sum the S partials of this column tile in split order
   for (int e = tid; e < n * kColTile; e += 256) {
     const int m = e / kColTile, c = c0 + e % kColTile;
     if (c < d) {
       float tot = 0.f;
-      for (int s2 = 0; s2 < S; ++s2) tot += part[((size_t)s2 * n + m) * d + c];
+      for (int s2 = 0; s2 < S; ++s2)
+        tot += __hip_atomic_load(&part[((size_t)s2 * n + m) * d + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       y[(size_t)m * d + c] = tot;
     }
   }

@@ -2,11 +2,15 @@
 // abstract and Figures 1-3): z = Q x (Q = V_r^T, [r, d] bf16), p = L z + b
 // (L = U_r diag(sigma_r), [f, r] bf16), candidates {i : p_i > tau_i}.
 //
-// Two launches. The first computes z with one wave per row of Q and clears the scan
-// state of the second. The second streams L in tiles of 64 rows, compares with tau and
-// writes the candidate list in ascending order with a single-pass decoupled look-back
-// scan over tile counts (tiles take dynamic tickets, so every predecessor a tile waits
-// on has already started and never waits on a later tile).
+// Two launches. The first computes z with two rows of Q per workgroup (256 threads per
+// row, 16 bytes each per pass) and clears the scan state of the second. The second
+// streams L in tiles of 64 rows, compares with tau and writes the candidate list in
+// ascending order with a single-pass decoupled look-back scan over tile counts. Tile =
+// workgroup index: workgroups are dispatched in index order, so every predecessor a tile
+// waits on has already started and never waits on a later tile. Each tile's status and
+// count share one 64-bit word, so
+// the look-back needs only relaxed device-scope atomics: no cache writeback or
+// invalidation (a release or acquire at device scope would flush the whole L2).
 
 #include "device_common.h"
 #include "kernels.h"
@@ -18,36 +22,43 @@ namespace {
 
 constexpr int kRowsPerTile = 64;
 
-struct SvdWs {
-  uint32_t ticket;
-  uint32_t pad[63];
-};
-
 // 64-bit tile word: status in the high half (0 none, 1 tile count, 2 inclusive prefix).
 __device__ __forceinline__ unsigned long long pack(uint32_t status, uint32_t v) {
   return ((unsigned long long)status << 32) | v;
 }
 
 __global__ __launch_bounds__(512) void svd_z_kernel(const char* __restrict__ q, const char* __restrict__ x, int d,
-                                                    int r, float* __restrict__ z, SvdWs* st,
+                                                    int r, float* __restrict__ z,
                                                     unsigned long long* flags, int ntiles) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 8 + (threadIdx.x >> 6);
+  __shared__ float part[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = tid >> 8, t = tid & 255;  // row of the pair, thread within the row
+  const int row = blockIdx.x * 2 + half;
   // scan state of the candidate pass
-  const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int gtid = blockIdx.x * blockDim.x + tid;
   for (int i = gtid; i < ntiles; i += gridDim.x * blockDim.x) flags[i] = 0ull;
-  if (gtid == 0) st->ticket = 0u;
-  if (row >= r) return;
   const int nch = d / 8;
   const size_t rb = (size_t)d * 2;
   float acc = 0.f;
-  for (int c = lane; c < nch; c += 64) {
-    const uint4 w = ldg16(q + (size_t)row * rb + (size_t)c * 16);
-    const uint4 xv = ld16(x + (size_t)c * 16);
-    acc = Chunk<WT_BF16>::dot(w, xv, acc);
+  if (row < r) {
+    constexpr int U = 4;  // chunks in flight per thread
+    for (int c0 = t; c0 < nch; c0 += 256 * U) {
+      uint4 w[U], xv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + 256 * u;
+        const bool ok = c < nch;
+        w[u] = ok ? ldg16(q + (size_t)row * rb + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
+        xv[u] = ok ? ld16(x + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc = Chunk<WT_BF16>::dot(w[u], xv[u], acc);
+    }
   }
   acc = wave_sum(acc);
-  if (lane == 0) z[row] = acc;
+  if (lane == 0) part[wave] = acc;
+  __syncthreads();
+  if (t == 0 && row < r) z[row] = part[4 * half] + part[4 * half + 1] + part[4 * half + 2] + part[4 * half + 3];
 }
 
 // 256 threads; each row of L (r bf16 = r/8 chunks) is handled by TPR = r/8 threads (r <= 512
@@ -56,16 +67,13 @@ template <int TPR>
 __global__ __launch_bounds__(256) void svd_p_kernel(const char* __restrict__ l, const float* __restrict__ z,
                                                     const float* __restrict__ bias, const float* __restrict__ tau,
                                                     int f, int r, int32_t* __restrict__ cand, int32_t* n_cand,
-                                                    float* __restrict__ p_out, SvdWs* st,
+                                                    float* __restrict__ p_out,
                                                     unsigned long long* flags, int ntiles) {
   constexpr int RPI = 256 / TPR;  // rows side by side
-  __shared__ uint32_t s_tile;
   __shared__ float s_p[kRowsPerTile];
   __shared__ uint32_t s_excl;
   const int tid = threadIdx.x;
-  if (tid == 0) s_tile = __hip_atomic_fetch_add(&st->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const int tile = (int)s_tile;
+  const int tile = blockIdx.x;
   const int row0 = tile * kRowsPerTile;
   const int rl = tid / TPR, cl = tid % TPR;
   const int nch = r / 8;
@@ -109,29 +117,43 @@ __global__ __launch_bounds__(256) void svd_p_kernel(const char* __restrict__ l, 
     const unsigned long long bal = __ballot(on);
     const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
     const uint32_t cnt = (uint32_t)__popcll(bal);
-    if (tid == 0) {
-      uint32_t excl = 0;
-      if (tile == 0) {
-        __hip_atomic_store(&flags[0], pack(2u, cnt), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      } else {
-        __hip_atomic_store(&flags[tile], pack(1u, cnt), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        int j = tile - 1;
-        while (j >= 0) {
-          unsigned long long fl;
-          uint32_t spins = 0;
-          do {
-            fl = __hip_atomic_load(&flags[j], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-            if ((fl >> 32) == 0ull) {
-              __builtin_amdgcn_s_sleep(1);
-              if (++spins > (1u << 24)) break;  // never expected: predecessors always finish
-            }
-          } while ((fl >> 32) == 0ull);
-          excl += (uint32_t)fl;
-          if ((fl >> 32) == 2ull || (fl >> 32) == 0ull) break;
-          --j;
+    // Look-back by the whole wave: lane l reads the word of tile (top - l), 64 at a time.
+    // The nearest tile with an inclusive prefix closes the window; tiles without any
+    // status yet are waited for (they have a lower index, so they are running).
+    uint32_t excl = 0;
+    if (tile == 0) {
+      if (tid == 0) __hip_atomic_store(&flags[0], pack(2u, cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (tid == 0) __hip_atomic_store(&flags[tile], pack(1u, cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int top = tile - 1;
+      uint32_t spins = 0;
+      while (top >= 0) {
+        const int j = top - tid;
+        unsigned long long fl = j >= 0 ? __hip_atomic_load(&flags[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                       : pack(2u, 0u);  // before tile 0: prefix 0
+        const uint32_t st = (uint32_t)(fl >> 32);
+        const unsigned long long done = __ballot(st == 2u);   // lanes holding a prefix
+        const unsigned long long none = __ballot(st == 0u);   // lanes not published yet
+        // lanes up to and including the nearest prefix (lowest lane index with st == 2)
+        const int stop = done ? __builtin_ctzll(done) : 64;
+        const unsigned long long need = stop >= 63 ? ~0ull : ((2ull << stop) - 1ull);
+        if (none & need) {  // some tile in the window is not published yet: read again
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > (1u << 24)) break;  // never expected: predecessors always finish
+          continue;
         }
-        __hip_atomic_store(&flags[tile], pack(2u, excl + cnt), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t v = (tid <= stop) ? (uint32_t)fl : 0u;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+        excl += v;
+        if (stop < 64) break;
+        top -= 64;
       }
+      if (tid == 0) {
+        __hip_atomic_store(&flags[tile], pack(2u, excl + cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (tid == 0) {
       s_excl = excl;
       if (tile == ntiles - 1) *n_cand = (int32_t)(excl + cnt);
     }
@@ -147,7 +169,7 @@ __global__ __launch_bounds__(256) void svd_p_kernel(const char* __restrict__ l, 
 size_t svd_workspace_bytes(int d, int f, int r) {
   (void)d;
   const int ntiles = (f + kRowsPerTile - 1) / kRowsPerTile;
-  size_t bytes = kWsHeader + sizeof(SvdWs);
+  size_t bytes = kWsHeader;
   bytes += (size_t)ntiles * sizeof(unsigned long long);
   bytes = (bytes + 255) & ~(size_t)255;
   bytes += (size_t)r * sizeof(float);
@@ -158,25 +180,24 @@ hipError_t launch_svd_predict(const sfn_svd& s, const void* x, int32_t* cand, in
                               void* ws, hipStream_t stream) {
   const int ntiles = (s.f + kRowsPerTile - 1) / kRowsPerTile;
   char* p = static_cast<char*>(ws) + kWsHeader;
-  SvdWs* st = reinterpret_cast<SvdWs*>(p);
-  unsigned long long* flags = reinterpret_cast<unsigned long long*>(p + sizeof(SvdWs));
-  size_t off = sizeof(SvdWs) + (size_t)ntiles * sizeof(unsigned long long);
+  unsigned long long* flags = reinterpret_cast<unsigned long long*>(p);
+  size_t off = (size_t)ntiles * sizeof(unsigned long long);
   off = (off + 255) & ~(size_t)255;
   float* z = reinterpret_cast<float*>(p + off);
-  hipLaunchKernelGGL(svd_z_kernel, dim3((s.r + 7) / 8), dim3(512), 0, stream, static_cast<const char*>(s.q),
-                     static_cast<const char*>(x), s.d, s.r, z, st, flags, ntiles);
+  hipLaunchKernelGGL(svd_z_kernel, dim3((s.r + 1) / 2), dim3(512), 0, stream, static_cast<const char*>(s.q),
+                     static_cast<const char*>(x), s.d, s.r, z, flags, ntiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nch = s.r / 8;
   const char* l = static_cast<const char*>(s.l);
   if (nch <= 8) {
-    hipLaunchKernelGGL((svd_p_kernel<8>), dim3(ntiles), dim3(256), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, st, flags, ntiles);
+    hipLaunchKernelGGL((svd_p_kernel<8>), dim3(ntiles), dim3(256), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
   } else if (nch <= 16) {
-    hipLaunchKernelGGL((svd_p_kernel<16>), dim3(ntiles), dim3(256), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, st, flags, ntiles);
+    hipLaunchKernelGGL((svd_p_kernel<16>), dim3(ntiles), dim3(256), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
   } else if (nch <= 32) {
-    hipLaunchKernelGGL((svd_p_kernel<32>), dim3(ntiles), dim3(256), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, st, flags, ntiles);
+    hipLaunchKernelGGL((svd_p_kernel<32>), dim3(ntiles), dim3(256), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
   } else if (nch <= 64) {
-    hipLaunchKernelGGL((svd_p_kernel<64>), dim3(ntiles), dim3(256), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, st, flags, ntiles);
+    hipLaunchKernelGGL((svd_p_kernel<64>), dim3(ntiles), dim3(256), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
   } else {
     return hipErrorInvalidValue;  // r > 512 needs more than one wave per row
   }
