@@ -171,7 +171,7 @@ def sparse_ffn_strerror(status: int) -> str:
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A zero-filled workspace of nbytes (the library's control words start at zero)."""
+    """A zero-filled workspace of nbytes (its reserved first 2 KiB must start at zero)."""
     if nbytes <= 0:
         raise ValueError("workspace size query failed (invalid arguments)")
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)

@@ -5,13 +5,17 @@
 //
 // Stage 1 (gate and up): H[m, i] = act(x_m . Wg[i] + b_i) * (x_m . Wu[i]) for 16 neurons
 // per workgroup. v_mfma_f32_16x16x32_bf16 takes the tokens as the M side and 16 neurons
-// as the N side; a lane's 8-element K fragment of a weight row is 16 contiguous bytes,
-// loaded straight from HBM. The four waves split K and combine through LDS. H is rounded
-// to bf16 for stage 2.
-// Stage 2 (down): Y = H Dt with Dt = W_down^T [f, d]. The K side (neurons) is the slow
-// axis of Dt, so 32x64 tiles of Dt are loaded coalesced, staged in LDS and read back
-// transposed into B fragments. K is split over S workgroups per 64-column tile; the last
-// of the S to finish adds the partials in a fixed order.
+// as the N side. A fragment of a weight row is 16 contiguous bytes, but one wave-wide
+// load of fragments would touch 16 rows at 64 bytes each, which HBM serves far below its
+// streaming rate; so the weights go through LDS: each stage loads 512-element (1 KB)
+// pieces of the 32 rows (Wg and Wu), one row per wave instruction, while the matrix
+// cores work on the previous stage. The four waves split each stage's K range and
+// combine through LDS at the end. H is rounded to bf16 for stage 2.
+// Stage 2 (down): Y = H Dt with Dt = W_down^T [f, d]. K (neurons) is the slow axis of
+// Dt: a workgroup owns 256 output columns and a range of K, loads 32 x 256 tiles (two
+// rows of 512 bytes per wave instruction), stages them in LDS and reads B fragments back
+// transposed. K is split over S workgroups per column tile; a third launch adds the S
+// partials in split order (deterministic), every output element in parallel.
 // Both stages are bound by HBM (16 tokens = 16 flop per weight byte).
 
 #include "device_common.h"
@@ -25,9 +29,11 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
-constexpr int kPF1 = 8;  // K steps (of 32) in flight per wave in stage 1
-constexpr int kPF2 = 8;  // K steps staged per batch in stage 2
-constexpr int kColTile = 64;
+constexpr int kKT = 512;           // stage 1: K elements per stage (1 KB of a bf16 row)
+constexpr int kLdsRow1 = kKT + 8;  // padded LDS row (elements)
+constexpr int kCT = 256;           // stage 2: output columns per workgroup
+constexpr int kLdsRow2 = kCT + 8;
+constexpr int kPB = 2;             // stage 2: K steps (of 32 rows) staged per batch
 
 __device__ __forceinline__ bf16x8_t as_frag(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -41,35 +47,60 @@ __global__ __launch_bounds__(256) void chunk_stage1_kernel(const char* __restric
                                                            const float* __restrict__ bias, const char* __restrict__ x,
                                                            int n, int d, int f, int act,
                                                            uint16_t* __restrict__ H) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[2][16][kLdsRow1];
   __shared__ f32x4_t s_part[4][2][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * 16;
   const int col = lane & 15, q = lane >> 4;
-  const int neuron = n0 + col;
-  const bool nrow_ok = neuron < f;
   const bool tok_ok = col < n;  // A side: lane's token is col
   const int hs = (f + 7) & ~7;  // H row stride (elements)
   const size_t rb = (size_t)d * 2;
-  const int nks = (d + 31) / 32;
-  const int ks0 = (int)((long long)wave * nks / 4), ks1 = (int)((long long)(wave + 1) * nks / 4);
-  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  const char* wg_row = wg + (size_t)neuron * rb;
-  const char* wu_row = wu + (size_t)neuron * rb;
-  const char* x_row = x + (size_t)col * rb;
-  for (int ks = ks0; ks < ks1; ks += kPF1) {
-    uint4 fa[kPF1], fg[kPF1], fu[kPF1];
+  const int nst = (d + kKT - 1) / kKT;
+  // loader: round i (0..7) of wave v reads row slot 4 i + v (matrix slot / 16, row slot % 16),
+  // bytes [16 lane, 16 lane + 16) of the stage's 1 KB piece
+  uint4 wr[8], xr[4], xc[4];
+  auto load = [&](int st) {
+    const int k = st * kKT + lane * 8;
+    const bool kok = k < d;
+    const size_t koff = (size_t)(kok ? k : 0) * 2;
 #pragma unroll
-    for (int p = 0; p < kPF1; ++p) {
-      const int k = (ks + p) * 32 + q * 8;
-      const bool kok = (ks + p) < ks1 && k < d;
-      fa[p] = (kok && tok_ok) ? ld16(x_row + (size_t)k * 2) : make_uint4(0, 0, 0, 0);
-      fg[p] = (kok && nrow_ok) ? ldg16(wg_row + (size_t)k * 2) : make_uint4(0, 0, 0, 0);
-      fu[p] = (kok && nrow_ok) ? ldg16(wu_row + (size_t)k * 2) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      const int slot = 4 * i + wave;
+      const int row = n0 + (slot & 15);
+      const bool ok = kok && row < f;
+      const char* base = (slot < 16 ? wg : wu) + (size_t)(row < f ? row : 0) * rb;
+      const uint4 v = ldg16(base + koff);
+      wr[i] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+    // A fragments of this wave's quarter: token col, K = st kKT + 128 wave + 32 t + 8 q
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int kx = st * kKT + 128 * wave + 32 * t + 8 * q;
+      const bool ok = tok_ok && kx < d;
+      const uint4 v = ld16(x + (size_t)(tok_ok ? col : 0) * rb + (size_t)(kx < d ? kx : 0) * 2);
+      xr[t] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+  };
+  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  load(0);
+  for (int st = 0; st < nst; ++st) {
+    __syncthreads();  // the previous stage's fragments have been read
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int slot = 4 * i + wave;
+      *reinterpret_cast<uint4*>(&s_w[slot >> 4][slot & 15][lane * 8]) = wr[i];
     }
 #pragma unroll
-    for (int p = 0; p < kPF1; ++p) {
-      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_frag(fa[p]), as_frag(fg[p]), accg, 0, 0, 0);
-      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_frag(fa[p]), as_frag(fu[p]), accu, 0, 0, 0);
+    for (int t = 0; t < 4; ++t) xc[t] = xr[t];
+    __syncthreads();
+    if (st + 1 < nst) load(st + 1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int kk = 128 * wave + 32 * t + 8 * q;
+      const uint4 bg = *reinterpret_cast<const uint4*>(&s_w[0][col][kk]);
+      const uint4 bu = *reinterpret_cast<const uint4*>(&s_w[1][col][kk]);
+      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_frag(xc[t]), as_frag(bg), accg, 0, 0, 0);
+      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_frag(xc[t]), as_frag(bu), accu, 0, 0, 0);
     }
   }
   s_part[wave][0][lane] = accg;
@@ -83,6 +114,8 @@ __global__ __launch_bounds__(256) void chunk_stage1_kernel(const char* __restric
       u += s_part[w][1][lane];
     }
     // lane holds tokens 4q + i (rows of C) for neuron n0 + col (column of C)
+    const int neuron = n0 + col;
+    const bool nrow_ok = neuron < f;
     const float bv = (bias && nrow_ok) ? bias[neuron] : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -100,105 +133,117 @@ __global__ __launch_bounds__(256) void chunk_stage1_kernel(const char* __restric
 
 __global__ __launch_bounds__(256) void chunk_stage2_kernel(const uint16_t* __restrict__ H, const char* __restrict__ wd,
                                                            int n, int d, int f, int S,
-                                                           float* __restrict__ part, uint32_t* __restrict__ arrive,
-                                                           float* __restrict__ y) {
-  __shared__ uint16_t s_dt[kPF2][32][kColTile + 8];
-  __shared__ uint32_t s_last;
+                                                           float* __restrict__ part, float* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_dt[kPB][32][kLdsRow2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ntile = (d + kColTile - 1) / kColTile;
+  const int ntile = (d + kCT - 1) / kCT;
   const int ct = blockIdx.x % ntile, s = blockIdx.x / ntile;
-  const int c0 = ct * kColTile;
+  const int c0 = ct * kCT;
   const int nks = (f + 31) / 32;
   const int ks0 = (int)((long long)s * nks / S), ks1 = (int)((long long)(s + 1) * nks / S);
   const size_t rb = (size_t)d * 2;
-  // loader mapping: thread -> (row tid/8 of the 32-row step, 8 columns at (tid%8)*8)
-  const int lr = tid >> 3, lc = (tid & 7) * 8;
-  const bool lcol_ok = c0 + lc < d;
+  // loader: K step p, round i (0..3): wave v reads rows 8 i + 2 v + (lane >> 5), bytes
+  // [16 (lane & 31), +16) of the 512-byte column range
+  const int lrow = 2 * wave + (lane >> 5), lch = (lane & 31) * 8;
+  const bool lcol_ok = c0 + lch < d;
+  const size_t lcoff = (size_t)(lcol_ok ? c0 + lch : 0) * 2;
   // fragment mapping
   const int col = lane & 15, q = lane >> 4;
   const bool tok_ok = col < n;
   const int hs = (f + 7) & ~7;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  uint4 stage[kPF2];
+  f32x4_t acc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 stage[kPB][4];
   auto load_batch = [&](int kb) {
 #pragma unroll
-    for (int p = 0; p < kPF2; ++p) {
-      const int row = (kb + p) * 32 + lr;
-      const bool ok = (kb + p) < ks1 && row < f && lcol_ok;
-      stage[p] = ok ? ldg16(wd + (size_t)row * rb + (size_t)(c0 + lc) * 2) : make_uint4(0, 0, 0, 0);
-    }
+    for (int p = 0; p < kPB; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = (kb + p) * 32 + 8 * i + lrow;
+        const bool ok = (kb + p) < ks1 && row < f && lcol_ok;
+        const uint4 v = ldg16(wd + (size_t)(row < f ? row : 0) * rb + lcoff);
+        stage[p][i] = ok ? v : make_uint4(0, 0, 0, 0);
+      }
   };
   load_batch(ks0);
-  for (int kb = ks0; kb < ks1; kb += kPF2) {
+  for (int kb = ks0; kb < ks1; kb += kPB) {
     __syncthreads();
 #pragma unroll
-    for (int p = 0; p < kPF2; ++p) *reinterpret_cast<uint4*>(&s_dt[p][lr][lc]) = stage[p];
-    __syncthreads();
-    if (kb + kPF2 < ks1) load_batch(kb + kPF2);
+    for (int p = 0; p < kPB; ++p)
 #pragma unroll
-    for (int p = 0; p < kPF2; ++p) {
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&s_dt[p][8 * i + lrow][lch]) = stage[p][i];
+    __syncthreads();
+    if (kb + kPB < ks1) load_batch(kb + kPB);
+#pragma unroll
+    for (int p = 0; p < kPB; ++p) {
       if (kb + p < ks1) {
         const int k = (kb + p) * 32 + q * 8;
         const uint4 a = (tok_ok && k < f) ? ld16(reinterpret_cast<const char*>(H + (size_t)col * hs + k))
                                           : make_uint4(0, 0, 0, 0);
-        // B fragment: Dt[k + j][c0 + 16 wave + col], j < 8, from the staged tile
-        uint32_t bw[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = s_dt[p][q * 8 + 2 * j][16 * wave + col];
-          const uint32_t hi = s_dt[p][q * 8 + 2 * j + 1][16 * wave + col];
-          bw[j] = lo | (hi << 16);
+        for (int b = 0; b < 4; ++b) {
+          // B fragment: Dt[k + j][c0 + 64 wave + 16 b + col], j < 8, from the staged tile
+          const int cc = 64 * wave + 16 * b + col;
+          uint32_t bw[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = s_dt[p][q * 8 + 2 * j][cc];
+            const uint32_t hi = s_dt[p][q * 8 + 2 * j + 1][cc];
+            bw[j] = lo | (hi << 16);
+          }
+          const uint4 bv = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_frag(a), as_frag(bv), acc[b], 0, 0, 0);
         }
-        const uint4 b = make_uint4(bw[0], bw[1], bw[2], bw[3]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_frag(a), as_frag(b), acc, 0, 0, 0);
       }
     }
   }
-  // C[4q + i][16 wave + col]: token 4q + i, column c0 + 16 wave + col
-  const int ycol = c0 + 16 * wave + col;
+  // C[4q + i][16 b + col] of block b: token 4q + i, column c0 + 64 wave + 16 b + col
   if (S == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * q + i;
-      if (m < n && ycol < d) y[(size_t)m * d + ycol] = acc[i];
+    for (int b = 0; b < 4; ++b) {
+      const int ycol = c0 + 64 * wave + 16 * b + col;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * q + i;
+        if (m < n && ycol < d) y[(size_t)m * d + ycol] = acc[b][i];
+      }
     }
     return;
   }
-  // Partials cross workgroups (and XCDs, whose L2s are not coherent with each other):
-  // they are written through to memory with relaxed device-scope stores and read back
-  // the same way, and the arrival ticket is a relaxed device-scope atomic. Nothing here
-  // needs a fence, which at device scope would write back the whole L2.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 4 * q + i;
-    if (m < n && ycol < d)
-      __hip_atomic_store(&part[((size_t)s * n + m) * d + ycol], acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial is in memory
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(&arrive[ct], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (old == (uint32_t)(S - 1)) ? 1u : 0u;
-    if (s_last) __hip_atomic_store(&arrive[ct], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // old >= S means the counter was not zero at launch; no tile is then summed
-  }
-  __syncthreads();
-  if (!s_last) return;
-  // sum the S partials of this column tile in split order
-  for (int e = tid; e < n * kColTile; e += 256) {
-    const int m = e / kColTile, c = c0 + e % kColTile;
-    if (c < d) {
-      float tot = 0.f;
-      for (int s2 = 0; s2 < S; ++s2)
-        tot += __hip_atomic_load(&part[((size_t)s2 * n + m) * d + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      y[(size_t)m * d + c] = tot;
+  for (int b = 0; b < 4; ++b) {
+    const int ycol = c0 + 64 * wave + 16 * b + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * q + i;
+      if (m < n && ycol < d) part[((size_t)s * n + m) * d + ycol] = acc[b][i];
     }
   }
 }
 
+// y = sum over the S splits of part[s, :, :], in split order; one float4 per thread.
+__global__ __launch_bounds__(256) void chunk_reduce_kernel(const float* __restrict__ part, int S, int n4,
+                                                           float* __restrict__ y) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= n4) return;
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(part) + e;
+  f32x4_t tot = {0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 8 <= S; s += 8) {
+    f32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(s + u) * n4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) tot += v[u];
+  }
+  for (; s < S; ++s) tot += src[(size_t)s * n4];
+  reinterpret_cast<f32x4_t*>(y)[e] = tot;
+}
+
 int chunk_splits(int d, int f) {
-  const int ntile = (d + kColTile - 1) / kColTile;
-  int S = (512 + ntile - 1) / ntile;
+  const int ntile = (d + kCT - 1) / kCT;
+  int S = (1024 + ntile - 1) / ntile;  // about 1024 workgroups
   const int maxs = (f + 255) / 256;
   if (S > maxs) S = maxs;
   return S < 1 ? 1 : S;
@@ -246,11 +291,9 @@ hipError_t launch_dense_chunk(const sfn_ffn& ffn, const void* x, int n, float* y
     }
     return hipSuccess;
   }
-  const int ntile = (ffn.d + kColTile - 1) / kColTile;
+  const int ntile = (ffn.d + kCT - 1) / kCT;
   const int S = chunk_splits(ffn.d, ffn.f);
-  if (ntile > kMaxColTiles) return hipErrorInvalidValue;
   char* p = static_cast<char*>(ws);
-  uint32_t* arrive = reinterpret_cast<uint32_t*>(p + kWsChunkCounters);
   size_t off = kWsHeader;
   uint16_t* H = reinterpret_cast<uint16_t*>(p + off);
   off += (size_t)SFN_MAX_CHUNK * ((ffn.f + 7) & ~7) * sizeof(uint16_t);
@@ -262,7 +305,11 @@ hipError_t launch_dense_chunk(const sfn_ffn& ffn, const void* x, int n, float* y
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(chunk_stage2_kernel, dim3(ntile * S), dim3(256), 0, stream, H,
-                     static_cast<const char*>(ffn.w_down_t), n, ffn.d, ffn.f, S, part, arrive, y);
+                     static_cast<const char*>(ffn.w_down_t), n, ffn.d, ffn.f, S, part, y);
+  if (S > 1) {
+    const int n4 = n * ffn.d / 4;
+    hipLaunchKernelGGL(chunk_reduce_kernel, dim3((n4 + 255) / 256), dim3(256), 0, stream, part, S, n4, y);
+  }
   return hipGetLastError();
 }
 

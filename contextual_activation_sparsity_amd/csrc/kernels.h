@@ -10,15 +10,12 @@
 namespace sfn {
 
 // Workspace layout shared by every call on a workspace:
-//   [0, 256)            reserved
-//   [256, 1280)         dense-chunk column-tile arrival counters (256 x uint32)
-//   [1280, kWsHeader)   reserved
+//   [0, kWsHeader)      reserved for words that persist between calls (none are used:
+//                       every cross-workgroup hand-off is a kernel boundary or lives in
+//                       per-call scratch); zero-filled once by the caller
 //   [kWsHeader, ...)    per-call scratch, rewritten by each call before it is read
-// The header is zero-filled once by the caller; each call leaves its counters at zero.
-// Scratch of one call may overlap scratch of another, never the header.
+// Scratch of one call may overlap scratch of another.
 constexpr size_t kWsHeader = 2048;
-constexpr size_t kWsChunkCounters = 256;
-constexpr int kMaxColTiles = 256;
 
 struct DecodeArgs {
   const char* wg;

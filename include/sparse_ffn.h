@@ -33,13 +33,12 @@
  *     which reports a launch error from the HIP runtime. Device-side faults surface at
  *     the caller's next synchronisation. No C++ exception crosses the ABI.
  *   - Workspace: `ws` of `ws_bytes` bytes (256-byte aligned), sized by the
- *     *_workspace_size queries. Its first 2 KiB hold control words that persist between
- *     calls (the dense chunk's column-tile arrival counters); everything after them is
- *     scratch each call rewrites before reading. It must be zero-filled once when it is
- *     allocated (e.g. torch.zeros); every call leaves its counters at zero again when
- *     it completes, so any sequence of calls on one stream may share one workspace
- *     (sized for the largest of them). Calls that may run concurrently (different
- *     streams) need distinct workspaces.
+ *     *_workspace_size queries. Its first 2 KiB are reserved and must be zero-filled
+ *     once when the workspace is allocated (e.g. torch.zeros); no call changes them.
+ *     Everything after them is scratch each call rewrites before reading, so any
+ *     sequence of calls on one stream may share one workspace (sized for the largest
+ *     of them). Calls that may run concurrently (different streams) need distinct
+ *     workspaces.
  *   - Outputs are deterministic: identical inputs give bitwise identical y, index
  *     lists and thresholds (fixed reduction orders, no floating-point atomics).
  *   - Arithmetic: products and sums in fp32 (bf16 inputs are widened exactly).

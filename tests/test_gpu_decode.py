@@ -28,7 +28,7 @@ def _tol(dtype):
 
 
 def _header_clear(ws):
-    """The first 2 KiB of a workspace hold counters that every call leaves at zero."""
+    """The first 2 KiB of a workspace are reserved: no call may change them."""
     return not bool(ws[:2048].any().item())
 
 
@@ -217,7 +217,7 @@ def test_candidate_mode_reglu():
 
 def test_one_workspace_shared_by_every_call():
     """calibrate -> decode -> dense chunk -> predictor -> decode -> calibrate -> decode on a
-    single workspace: each call must leave the persistent control words as it found them
+    single workspace: each call must leave the reserved header as it found it
     (regression: the calibration state once overlapped a decode counter)."""
     w = inputs.workload(1)
     d, f, n_cal = 2048, 3000, 64
