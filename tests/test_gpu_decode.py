@@ -112,6 +112,12 @@ def test_llama2_7b_layer(k):
     _case(w, w.d, w.f, k, 4)
 
 
+def test_llama3_70b_layer():
+    """Full Llama-3-70B FFN shape (d 8192: two 16-byte chunks per thread and row)."""
+    w = inputs.workload(4)
+    _case(w, w.d, w.f, 0.5, 2)
+
+
 def test_batch4_union_llama3_8b_layer():
     w = inputs.workload(2)
     layer, ws, dev, host, t = _case(w, w.d, w.f, 0.5, 8, batch=4)

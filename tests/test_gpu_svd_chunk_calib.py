@@ -94,7 +94,7 @@ def test_svd_sequential_pipeline_end_to_end():
 
 # ---------------------------------------------------------------------------- chunk
 @pytest.mark.parametrize("d,f,n", [(4096, 11008, 16), (1024, 3000, 5), (512, 1001, 1), (8192, 2048, 16),
-                                   (2048, 4100, 9)])
+                                   (2048, 4100, 9), (8192, 28672, 16), (4096, 11008, 1)])
 def test_dense_chunk_bf16(d, f, n):
     w = inputs.workload(4)
     say(f"[chunk] d={d} f={f} n={n}")
