@@ -2,8 +2,12 @@
 // Large Language Models", abstract: one threshold per layer sets the activation
 // sparsity). Offline: run once per layer, not on the decode path.
 //
-// 1. Scores S[m, i] = |act(x_m . Wg[i] + b_i)| for n calibration tokens, fp32, with an
-//    LDS-tiled vector kernel (16 tokens x 64 neurons per workgroup).
+// 1. Scores S[m, i] = |act(x_m . Wg[i] + b_i)| for n calibration tokens, fp32. bf16
+//    weights run on matrix cores (v_mfma_f32_16x16x32_bf16, 16 neurons per workgroup as
+//    the N side, 256 tokens per pass as 16 blocks of M): Wg goes through LDS in 1 KB row
+//    pieces, the token fragments come from L2, each wave owns 4 token blocks over the
+//    whole K range (no cross-wave sums). fp32 weights use an LDS-tiled vector kernel
+//    (16 tokens x 64 neurons per workgroup).
 // 2. The K-th smallest score by radix select: non-negative fp32 values order like their
 //    bit patterns read as uint32, so four passes of 8-bit digit histograms (most
 //    significant first) pin down the exact bit pattern. Each pass is a histogram kernel
@@ -26,13 +30,14 @@ struct SelState {
 };
 
 constexpr int kTokTile = 16, kNeurTile = 64, kKTile = 64;
+constexpr int kKT = 512;          // matrix-core scores: K elements per stage (1 KB of a bf16 row)
+constexpr int kTokPass = 256;     // tokens per workgroup (16 blocks of 16)
 
-template <int WT>
-__global__ __launch_bounds__(256) void score_kernel(const char* __restrict__ wg, const float* __restrict__ bias,
-                                                    const char* __restrict__ x, int n, int d, int f, int act,
-                                                    float* __restrict__ S, SelState* st, uint32_t K) {
-  __shared__ float s_w[kNeurTile][kKTile + 1];
-  __shared__ float s_x[kTokTile][kKTile + 1];
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+
+__device__ __forceinline__ bf16x8_t as_frag(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ void init_select(SelState* st, uint32_t K) {
   const int tid = threadIdx.x;
   if (blockIdx.x == 0 && blockIdx.y == 0) {
     st->hist[tid] = 0u;
@@ -41,6 +46,89 @@ __global__ __launch_bounds__(256) void score_kernel(const char* __restrict__ wg,
       st->k_rem = K;
     }
   }
+}
+
+__global__ __launch_bounds__(256) void score_mfma_kernel(const char* __restrict__ wg, const float* __restrict__ bias,
+                                                         const char* __restrict__ x, int n, int d, int f, int act,
+                                                         float* __restrict__ S, SelState* st, uint32_t K) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[16][kKT + 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  init_select(st, K);
+  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * kTokPass;
+  const int col = lane & 15, q = lane >> 4;
+  const size_t rb = (size_t)d * 2;
+  const int nst = (d + kKT - 1) / kKT;
+  // this wave's token blocks: m0 + 16 (wave + 4 b) + col for b < 4
+  const char* xrow[4];
+  bool tok_ok[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int m = m0 + 16 * (wave + 4 * b) + col;
+    tok_ok[b] = m < n;
+    xrow[b] = x + (size_t)(tok_ok[b] ? m : 0) * rb;
+  }
+  // loader: round i (0..3) of wave v reads row 4 i + v, bytes [16 lane, +16) of the 1 KB piece
+  uint4 wr[4];
+  auto load = [&](int stg) {
+    const int k = stg * kKT + lane * 8;
+    const size_t koff = (size_t)(k < d ? k : 0) * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = n0 + 4 * i + wave;
+      const uint4 v = ldg16(wg + (size_t)(row < f ? row : 0) * rb + koff);
+      wr[i] = (k < d && row < f) ? v : make_uint4(0, 0, 0, 0);
+    }
+  };
+  f32x4_t acc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  load(0);
+  for (int stg = 0; stg < nst; ++stg) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&s_w[4 * i + wave][lane * 8]) = wr[i];
+    __syncthreads();
+    if (stg + 1 < nst) load(stg + 1);
+    for (int t = 0; t < kKT / 32; ++t) {
+      const int kk = t * 32 + q * 8;
+      const int kx = stg * kKT + kk;
+      const uint4 bw = *reinterpret_cast<const uint4*>(&s_w[col][kk]);
+      uint4 xa[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint4 v = ld16(xrow[b] + (size_t)(kx < d ? kx : 0) * 2);
+        xa[b] = (tok_ok[b] && kx < d) ? v : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_frag(xa[b]), as_frag(bw), acc[b], 0, 0, 0);
+    }
+  }
+  // acc[b][i]: token m0 + 16 (wave + 4 b) + 4 q + i, neuron n0 + col
+  const int i0 = n0 + col;
+  if (i0 < f) {
+    const float bv = bias ? bias[i0] : 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 16 * (wave + 4 * b) + 4 * q + i;
+        if (m < n) {
+          const float g = acc[b][i] + bv;
+          const float a = act == 0 ? silu_f(g) : fmaxf(g, 0.f);
+          S[(size_t)m * f + i0] = fabsf(a);
+        }
+      }
+  }
+}
+
+template <int WT>
+__global__ __launch_bounds__(256) void score_kernel(const char* __restrict__ wg, const float* __restrict__ bias,
+                                                    const char* __restrict__ x, int n, int d, int f, int act,
+                                                    float* __restrict__ S, SelState* st, uint32_t K) {
+  __shared__ float s_w[kNeurTile][kKTile + 1];
+  __shared__ float s_x[kTokTile][kKTile + 1];
+  const int tid = threadIdx.x;
+  init_select(st, K);
   const int i0 = blockIdx.x * kNeurTile, m0 = blockIdx.y * kTokTile;
   const int j = tid % kNeurTile, tg = tid / kNeurTile;  // neuron j, tokens tg*4 .. tg*4+3
   constexpr int wb = WT == WT_BF16 ? 2 : 4;
@@ -155,11 +243,12 @@ hipError_t launch_calibrate(const sfn_ffn& ffn, const void* x_cal, int n, float 
   SelState* st = reinterpret_cast<SelState*>(static_cast<char*>(ws) + kWsHeader);
   float* S = scores_out ? scores_out
                         : reinterpret_cast<float*>(static_cast<char*>(ws) + kWsHeader + sizeof(SelState));
-  const dim3 sgrid((ffn.f + kNeurTile - 1) / kNeurTile, (n + kTokTile - 1) / kTokTile);
   if (ffn.wdtype == SFN_BF16) {
-    hipLaunchKernelGGL(score_kernel<WT_BF16>, sgrid, dim3(256), 0, stream, static_cast<const char*>(ffn.w_gate),
+    const dim3 mgrid((ffn.f + 15) / 16, (n + kTokPass - 1) / kTokPass);
+    hipLaunchKernelGGL(score_mfma_kernel, mgrid, dim3(256), 0, stream, static_cast<const char*>(ffn.w_gate),
                        ffn.b_gate, static_cast<const char*>(x_cal), n, ffn.d, ffn.f, ffn.act, S, st, (uint32_t)K);
   } else {
+    const dim3 sgrid((ffn.f + kNeurTile - 1) / kNeurTile, (n + kTokTile - 1) / kTokTile);
     hipLaunchKernelGGL(score_kernel<WT_F32>, sgrid, dim3(256), 0, stream, static_cast<const char*>(ffn.w_gate),
                        ffn.b_gate, static_cast<const char*>(x_cal), n, ffn.d, ffn.f, ffn.act, S, st, (uint32_t)K);
   }

@@ -76,6 +76,12 @@ __global__ __launch_bounds__(256) void svd_p_kernel(const char* __restrict__ l, 
   const int tile = blockIdx.x;
   const int row0 = tile * kRowsPerTile;
   const int rl = tid / TPR, cl = tid % TPR;
+  // wave 0: bias and threshold of row (row0 + lane), read now so the compare need not wait
+  float pb = 0.f, pt = 0.f;
+  if (tid < 64 && row0 + tid < f) {
+    pb = bias ? bias[row0 + tid] : 0.f;
+    pt = tau[row0 + tid];
+  }
   const int nch = r / 8;
   // z chunk of this lane, widened to fp32
   float zc[8];
@@ -110,9 +116,9 @@ __global__ __launch_bounds__(256) void svd_p_kernel(const char* __restrict__ l, 
     const int row = row0 + tid;
     bool on = false;
     if (row < f) {
-      const float p = s_p[tid] + (bias ? bias[row] : 0.f);
+      const float p = s_p[tid] + pb;
       if (p_out) p_out[row] = p;
-      on = p > tau[row];
+      on = p > pt;
     }
     const unsigned long long bal = __ballot(on);
     const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
