@@ -96,9 +96,15 @@ def _csv_rows(d, suffix):
     return rows
 
 
-def _short(name):
-    for k in DECODE_KERNELS + ("chunk_stage1_kernel", "chunk_stage2_kernel", "score_kernel", "hist_kernel",
-                               "pick_kernel", "svd_z_kernel", "svd_p_kernel"):
+def _short(name, keep_args=False):
+    if keep_args:
+        import re
+        m = re.search(r"(\w+_kernel)(<[^>]*>)?\(", name.replace("(anonymous namespace)::", ""))
+        if m and "sfn::" in name:
+            return m.group(1) + (m.group(2) or "").replace(" ", "")
+    for k in DECODE_KERNELS + ("chunk_stage1_kernel", "chunk_stage2_kernel", "chunk_reduce_kernel",
+                               "score_mfma_kernel", "score_kernel", "hist_kernel", "pick_kernel", "set_kernel",
+                               "svd_z_kernel", "svd_p_kernel"):
         if k in name:
             return k
     if "elementwise_kernel" in name and "neg" in name.lower():
@@ -107,19 +113,31 @@ def _short(name):
 
 
 def summarize_trace(d, command):
-    rows = _csv_rows(d, "kernel_stats.csv")
-    out = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", command or "(not recorded)", "```", "",
-           "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    """Markdown table of the library's kernels from a rocprofv3 --kernel-trace CSV output:
+    dispatches grouped by kernel and grid size (one group per shape), then torch's own
+    kernels (weight generation and the like) in one line."""
+    import statistics
+    rows = _csv_rows(d, "kernel_trace.csv")
+    groups, other_n, other_ns = {}, 0, 0.0
     for r in rows:
-        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
-    avg = {_short(r["Name"]): float(r["AverageNs"]) / 1e3 for r in rows}
-    if all(k in avg for k in DECODE_KERNELS):
-        out += ["", "One sparse_ffn_decode call is one dispatch of each decode kernel: "
-                f"{' + '.join(f'{avg[k]:.2f}' for k in DECODE_KERNELS)} = "
-                f"{sum(avg[k] for k in DECODE_KERNELS):.2f} us of kernel time per call. "
-                "bench.py also times calls that request no output, which run the gate kernel alone, "
-                "so that kernel has more dispatches than the other two."]
+        name = r["Kernel_Name"]
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if "sfn::" not in name:
+            other_n += 1
+            other_ns += dur
+            continue
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        wgs = grid // max(1, int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"]))
+        groups.setdefault((_short(name, keep_args=True), wgs, int(r["Workgroup_Size_X"])), []).append(dur)
+    out = ["# rocprofv3 kernel trace summary", "", "Command:", "", "```", command or "(not recorded)", "```", "",
+           "Template arguments of the decode kernels: <weight dtype (1 bf16, 0 fp32), tokens held (1 or 4), "
+           "16-byte chunks per thread, threads per row, rows per thread per step>.", "",
+           "| kernel | workgroups x threads | dispatches | average us | median us | min us | max us |",
+           "|---|---|---|---|---|---|---|"]
+    for (k, wgs, wgsz), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| `{k}` | {wgs} x {wgsz} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} | "
+                   f"{min(v):.2f} | {max(v):.2f} |")
+    out.append(f"| (torch kernels: input generation, copies) | | {other_n} | {other_ns / max(1, other_n):.2f} | | | |")
     print("\n".join(out))
 
 
