@@ -349,38 +349,14 @@ struct UpDownKernel {
   static constexpr int RPG = S::RPG, RG = S::RG, VU = S::VU, KV = S::KV;
 
   struct Smem {
+    int qslot[kTMax];         // list slot of each entry of this workgroup's share
     int qrow[kTMax];          // global row of each entry of this workgroup's share
     float qa[kTMax][BMAX];    // activations
     uint8_t qbits[kTMax];     // per-token mask bits
-    int pref[kGMax + 1];      // exclusive prefix of the tile counts
     float wpart[kNW][VU];
     float h[64][BMAX];
     int wsum[kNW];
   };
-
-  // Exclusive prefix of tile_cnt[i * kCnt + off] over the G tiles into sm.pref[0..G].
-  __device__ __forceinline__ static void tile_prefix(const DevArgs& a, Smem& sm, int off) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // each thread owns two consecutive tiles; G <= 1024 = 2 * kNT
-    const int i0 = 2 * tid;
-    const int c0 = i0 < a.G ? a.tile_cnt[i0 * kCnt + off] : 0;
-    const int c1 = i0 + 1 < a.G ? a.tile_cnt[(i0 + 1) * kCnt + off] : 0;
-    int v = c0 + c1;  // inclusive scan over the wave
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const int u = __shfl_up(v, m, 64);
-      if (lane >= m) v += u;
-    }
-    if (lane == 63) sm.wsum[wave] = v;
-    __syncthreads();
-    int base = 0;
-    for (int i = 0; i < wave; ++i) base += sm.wsum[i];
-    const int incl = base + v;
-    if (i0 <= a.G) sm.pref[i0] = incl - c0 - c1;
-    if (i0 + 1 <= a.G) sm.pref[i0 + 1] = incl - c1;
-    if (tid == kNT - 1 && a.G == 2 * kNT) sm.pref[a.G] = incl;  // the one slot no pair covers
-    __syncthreads();
-  }
 
   // Loads of one up/down step: w0 = Wu rows, w1 = Dt rows of share entries [base,
   // base+n), or (step none) both from x, L1-resident, results unused.
@@ -425,20 +401,47 @@ struct UpDownKernel {
         for (int v = 0; v < KV; ++v) acc[b][c][v] = 0.f;
 
     if (want_y) {
-      // ---- this workgroup's equal share of the concatenated active lists
-      tile_prefix(a, sm, 0);
-      const int n = sm.pref[a.G];
-      const int s0 = share_begin(w, n, a.G);
-      const int nq = share_begin(w + 1, n, a.G) - s0;
-      for (int j = tid; j < nq; j += kNT) {
-        const int pos = s0 + j;
-        int lo = 0, hi = a.G;  // largest tile t with pref[t] <= pos
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (sm.pref[mid] <= pos) lo = mid;
-          else hi = mid;
+      // ---- this workgroup's equal share [s0, s0 + nq) of the concatenated active lists.
+      // Each thread owns two consecutive tiles; a scan of the tile counts tells it where
+      // their lists sit in the concatenation and the total n, so it can mark, for each
+      // share entry inside its tiles, which list slot holds it. Then every thread copies
+      // one entry.
+      int n, s0, nq;
+      {
+        const int i0 = 2 * tid;  // G <= 1024 = 2 * kNT
+        const int c0 = i0 < a.G ? a.tile_cnt[i0 * kCnt] : 0;
+        const int c1 = i0 + 1 < a.G ? a.tile_cnt[(i0 + 1) * kCnt] : 0;
+        int v = c0 + c1;  // inclusive scan over the wave
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+          const int u = __shfl_up(v, m, 64);
+          if (lane >= m) v += u;
         }
-        const int o = share_begin(lo, n_total, a.G) + (pos - sm.pref[lo]);
+        if (lane == 63) sm.wsum[wave] = v;
+        __syncthreads();
+        int base = 0;
+        n = 0;
+#pragma unroll
+        for (int i = 0; i < kNW; ++i) {
+          const int ws = sm.wsum[i];
+          base += i < wave ? ws : 0;
+          n += ws;
+        }
+        s0 = share_begin(w, n, a.G);
+        nq = share_begin(w + 1, n, a.G) - s0;
+        int p0 = base + v - c0 - c1;  // first position of tile i0's list
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int cnt = t ? c1 : c0;
+          const int lo = max(p0, s0), hi = min(p0 + cnt, s0 + nq);
+          const int ob = share_begin(i0 + t, n_total, a.G) - p0;  // list slot = ob + position
+          for (int pos = lo; pos < hi; ++pos) sm.qslot[pos - s0] = ob + pos;
+          p0 += cnt;
+        }
+      }
+      __syncthreads();
+      for (int j = tid; j < nq; j += kNT) {
+        const int o = sm.qslot[j];
         sm.qrow[j] = a.sel_idx[o];
         sm.qbits[j] = a.sel_bits[o];
 #pragma unroll
