@@ -5,12 +5,12 @@
 // Two launches. The first computes z with two rows of Q per workgroup (256 threads per
 // row, 16 bytes each per pass) and clears the scan state of the second. The second
 // streams L in tiles of 64 rows, compares with tau and writes the candidate list in
-// ascending order with a single-pass decoupled look-back scan over tile counts. Tile =
-// workgroup index: workgroups are dispatched in index order, so every predecessor a tile
-// waits on has already started and never waits on a later tile. Each tile's status and
-// count share one 64-bit word, so
-// the look-back needs only relaxed device-scope atomics: no cache writeback or
-// invalidation (a release or acquire at device scope would flush the whole L2).
+// ascending order: each tile publishes its candidate count in a 64-bit word (a status in
+// the high half), then sums the counts of all lower tiles to find where its candidates
+// go. Tile = workgroup index: workgroups are dispatched in index order, so every tile
+// waited on has already started. Relaxed device-scope atomics suffice: no cache
+// writeback or invalidation (a release or acquire at device scope would flush the whole
+// L2).
 
 #include "device_common.h"
 #include "kernels.h"
@@ -22,7 +22,7 @@ namespace {
 
 constexpr int kRowsPerTile = 64;
 
-// 64-bit tile word: status in the high half (0 none, 1 tile count, 2 inclusive prefix).
+// 64-bit tile word: status in the high half (0 not yet published, 1 count published).
 __device__ __forceinline__ unsigned long long pack(uint32_t status, uint32_t v) {
   return ((unsigned long long)status << 32) | v;
 }
@@ -61,41 +61,45 @@ __global__ __launch_bounds__(512) void svd_z_kernel(const char* __restrict__ q, 
   if (t == 0 && row < r) z[row] = part[4 * half] + part[4 * half + 1] + part[4 * half + 2] + part[4 * half + 3];
 }
 
-// 256 threads; each row of L (r bf16 = r/8 chunks) is handled by TPR = r/8 threads (r <= 512
-// -> TPR <= 64 lanes of one wave); rows side by side = 256 / TPR.
+// 512 threads, kRowsPerTile rows of L per tile; each row (r bf16 = r/8 chunks) is handled
+// by TPR = r/8 threads (r <= 512 -> TPR <= 64 lanes of one wave), 512 / TPR rows side by
+// side. One wave per 64 rows then compares and compacts.
 template <int TPR>
-__global__ __launch_bounds__(256) void svd_p_kernel(const char* __restrict__ l, const float* __restrict__ z,
+__global__ __launch_bounds__(512) void svd_p_kernel(const char* __restrict__ l, const float* __restrict__ z,
                                                     const float* __restrict__ bias, const float* __restrict__ tau,
                                                     int f, int r, int32_t* __restrict__ cand, int32_t* n_cand,
                                                     float* __restrict__ p_out,
                                                     unsigned long long* flags, int ntiles) {
-  constexpr int RPI = 256 / TPR;  // rows side by side
+  constexpr int RPI = 512 / TPR;  // rows side by side
+  constexpr int NIT = kRowsPerTile / RPI;
+  constexpr int NCW = kRowsPerTile / 64;  // comparing waves
+  static_assert(kRowsPerTile % 64 == 0 && NCW <= 512 / 64, "whole waves compare the tile's rows");
   __shared__ float s_p[kRowsPerTile];
+  __shared__ uint32_t s_cnt[NCW];
   __shared__ uint32_t s_excl;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x;
   const int row0 = tile * kRowsPerTile;
   const int rl = tid / TPR, cl = tid % TPR;
-  // wave 0: bias and threshold of row (row0 + lane), read now so the compare need not wait
+  // waves 0-3: bias and threshold of row (row0 + tid), read now so the compare need not wait
   float pb = 0.f, pt = 0.f;
-  if (tid < 64 && row0 + tid < f) {
+  if (tid < kRowsPerTile && row0 + tid < f) {
     pb = bias ? bias[row0 + tid] : 0.f;
     pt = tau[row0 + tid];
   }
   const int nch = r / 8;
-  // z chunk of this lane, widened to fp32
-  float zc[8];
   const bool chunk_ok = cl < nch;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) zc[j] = chunk_ok ? z[cl * 8 + j] : 0.f;
   const size_t rb = (size_t)r * 2;
-  constexpr int NIT = kRowsPerTile / RPI;
   uint4 wv[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int row = row0 + rl + RPI * it;
     wv[it] = (chunk_ok && row < f) ? ldg16(l + (size_t)row * rb + (size_t)cl * 16) : make_uint4(0, 0, 0, 0);
   }
+  // z chunk of this lane, widened to fp32
+  float zc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) zc[j] = chunk_ok ? z[cl * 8 + j] : 0.f;
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const uint32_t p4[4] = {wv[it].x, wv[it].y, wv[it].z, wv[it].w};
@@ -111,62 +115,60 @@ __global__ __launch_bounds__(256) void svd_p_kernel(const char* __restrict__ l, 
     if (cl == 0) s_p[rl + RPI * it] = acc;
   }
   __syncthreads();
-  // wave 0: compare, ballot-compact, look back
-  if (tid < 64) {
-    const int row = row0 + tid;
-    bool on = false;
+  // waves 0 .. NCW-1: compare and ballot-compact 64 rows each
+  const int row = row0 + tid;
+  bool on = false;
+  unsigned long long bal = 0ull;
+  if (wave < NCW) {
     if (row < f) {
       const float p = s_p[tid] + pb;
       if (p_out) p_out[row] = p;
       on = p > pt;
     }
-    const unsigned long long bal = __ballot(on);
-    const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-    const uint32_t cnt = (uint32_t)__popcll(bal);
-    // Look-back by the whole wave: lane l reads the word of tile (top - l), 64 at a time.
-    // The nearest tile with an inclusive prefix closes the window; tiles without any
-    // status yet are waited for (they have a lower index, so they are running).
-    uint32_t excl = 0;
-    if (tile == 0) {
-      if (tid == 0) __hip_atomic_store(&flags[0], pack(2u, cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      if (tid == 0) __hip_atomic_store(&flags[tile], pack(1u, cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      int top = tile - 1;
-      uint32_t spins = 0;
-      while (top >= 0) {
-        const int j = top - tid;
-        unsigned long long fl = j >= 0 ? __hip_atomic_load(&flags[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                       : pack(2u, 0u);  // before tile 0: prefix 0
-        const uint32_t st = (uint32_t)(fl >> 32);
-        const unsigned long long done = __ballot(st == 2u);   // lanes holding a prefix
-        const unsigned long long none = __ballot(st == 0u);   // lanes not published yet
-        // lanes up to and including the nearest prefix (lowest lane index with st == 2)
-        const int stop = done ? __builtin_ctzll(done) : 64;
-        const unsigned long long need = stop >= 63 ? ~0ull : ((2ull << stop) - 1ull);
-        if (none & need) {  // some tile in the window is not published yet: read again
-          __builtin_amdgcn_s_sleep(1);
-          if (++spins > (1u << 24)) break;  // never expected: predecessors always finish
-          continue;
-        }
-        uint32_t v = (tid <= stop) ? (uint32_t)fl : 0u;
+    bal = __ballot(on);
+    if (lane == 0) s_cnt[wave] = (uint32_t)__popcll(bal);
+  }
+  __syncthreads();
+  uint32_t cnt = 0;
 #pragma unroll
-        for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-        excl += v;
-        if (stop < 64) break;
-        top -= 64;
+  for (int w2 = 0; w2 < NCW; ++w2) cnt += s_cnt[w2];
+  // Prefix over tiles: every tile publishes its count as soon as it has it; wave 0 then
+  // reads the counts of all lower tiles (four per lane in flight, waiting for any not yet
+  // published: lower tiles have lower workgroup indices, so they are running) and sums
+  // them. No tile waits on another tile's prefix, so there is no chain of round trips.
+  if (wave == 0) {
+    if (lane == 0) __hip_atomic_store(&flags[tile], pack(1u, cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t excl = 0;
+    for (int b0 = 0; b0 < tile; b0 += 256) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = b0 + 64 * u + lane;
+        if (j < tile) {
+          unsigned long long fl;
+          uint32_t spins = 0;
+          while (((fl = __hip_atomic_load(&flags[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 32) == 0ull) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins > (1u << 24)) break;  // never expected: lower tiles always publish
+          }
+          v += (uint32_t)fl;
+        }
       }
-      if (tid == 0) {
-        __hip_atomic_store(&flags[tile], pack(2u, excl + cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+      excl += v;
     }
-    if (tid == 0) {
+    if (lane == 0) {
       s_excl = excl;
       if (tile == ntiles - 1) *n_cand = (int32_t)(excl + cnt);
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const uint32_t base = s_excl;
-    if (on) cand[base + pos] = row;
+  }
+  __syncthreads();
+  if (on) {
+    uint32_t base = s_excl;
+    for (int w2 = 0; w2 < wave; ++w2) base += s_cnt[w2];
+    const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+    cand[base + pos] = row;
   }
 }
 
@@ -197,13 +199,13 @@ hipError_t launch_svd_predict(const sfn_svd& s, const void* x, int32_t* cand, in
   const int nch = s.r / 8;
   const char* l = static_cast<const char*>(s.l);
   if (nch <= 8) {
-    hipLaunchKernelGGL((svd_p_kernel<8>), dim3(ntiles), dim3(256), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
+    hipLaunchKernelGGL((svd_p_kernel<8>), dim3(ntiles), dim3(512), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
   } else if (nch <= 16) {
-    hipLaunchKernelGGL((svd_p_kernel<16>), dim3(ntiles), dim3(256), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
+    hipLaunchKernelGGL((svd_p_kernel<16>), dim3(ntiles), dim3(512), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
   } else if (nch <= 32) {
-    hipLaunchKernelGGL((svd_p_kernel<32>), dim3(ntiles), dim3(256), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
+    hipLaunchKernelGGL((svd_p_kernel<32>), dim3(ntiles), dim3(512), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
   } else if (nch <= 64) {
-    hipLaunchKernelGGL((svd_p_kernel<64>), dim3(ntiles), dim3(256), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
+    hipLaunchKernelGGL((svd_p_kernel<64>), dim3(ntiles), dim3(512), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
   } else {
     return hipErrorInvalidValue;  // r > 512 needs more than one wave per row
   }
