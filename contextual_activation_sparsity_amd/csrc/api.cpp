@@ -38,7 +38,7 @@ int check_svd(const sfn_svd* s) {
   if (!s) return SFN_EINVAL;
   if (s->reserved != 0) return SFN_EINVAL;
   if (s->d < 1 || s->d > SFN_MAX_D || s->f < 1 || s->f > SFN_MAX_F) return SFN_ESHAPE;
-  if (s->r < 1 || s->r > 512 || s->r > s->d) return SFN_ESHAPE;
+  if (s->r < 1 || s->r > SFN_MAX_RANK || s->r > s->d) return SFN_ESHAPE;
   if (s->d % 8 != 0 || s->r % 8 != 0) return SFN_EALIGN;
   if (!s->q || !s->l || !s->tau) return SFN_EINVAL;
   if (!aligned16(s->q) || !aligned16(s->l)) return SFN_EALIGN;

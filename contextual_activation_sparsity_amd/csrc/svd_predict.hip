@@ -61,10 +61,11 @@ __global__ __launch_bounds__(512) void svd_z_kernel(const char* __restrict__ q, 
   if (t == 0 && row < r) z[row] = part[4 * half] + part[4 * half + 1] + part[4 * half + 2] + part[4 * half + 3];
 }
 
-// 512 threads, kRowsPerTile rows of L per tile; each row (r bf16 = r/8 chunks) is handled
-// by TPR = r/8 threads (r <= 512 -> TPR <= 64 lanes of one wave), 512 / TPR rows side by
-// side. One wave per 64 rows then compares and compacts.
-template <int TPR>
+// 512 threads, kRowsPerTile rows of L per tile; each row (r bf16 = r/8 chunks of 16
+// bytes) is handled by TPR <= 64 lanes of one wave, CH chunks each (TPR CH >= r/8, so
+// r <= 1024), 512 / TPR rows side by side. One wave per 64 rows then compares and
+// compacts.
+template <int TPR, int CH>
 __global__ __launch_bounds__(512) void svd_p_kernel(const char* __restrict__ l, const float* __restrict__ z,
                                                     const float* __restrict__ bias, const float* __restrict__ tau,
                                                     int f, int r, int32_t* __restrict__ cand, int32_t* n_cand,
@@ -88,26 +89,34 @@ __global__ __launch_bounds__(512) void svd_p_kernel(const char* __restrict__ l, 
     pt = tau[row0 + tid];
   }
   const int nch = r / 8;
-  const bool chunk_ok = cl < nch;
   const size_t rb = (size_t)r * 2;
-  uint4 wv[NIT];
+  uint4 wv[NIT][CH];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int row = row0 + rl + RPI * it;
-    wv[it] = (chunk_ok && row < f) ? ldg16(l + (size_t)row * rb + (size_t)cl * 16) : make_uint4(0, 0, 0, 0);
-  }
-  // z chunk of this lane, widened to fp32
-  float zc[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) zc[j] = chunk_ok ? z[cl * 8 + j] : 0.f;
+    for (int c = 0; c < CH; ++c) {
+      const int ch = cl + TPR * c;
+      wv[it][c] = (ch < nch && row < f) ? ldg16(l + (size_t)row * rb + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  // z chunks of this lane, widened to fp32
+  float zc[CH][8];
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) zc[c][j] = cl + TPR * c < nch ? z[(cl + TPR * c) * 8 + j] : 0.f;
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    const uint32_t p4[4] = {wv[it].x, wv[it].y, wv[it].z, wv[it].w};
     float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc = fmaf(__uint_as_float(p4[j] << 16), zc[2 * j], acc);
-      acc = fmaf(__uint_as_float(p4[j] & 0xffff0000u), zc[2 * j + 1], acc);
+    for (int c = 0; c < CH; ++c) {
+      const uint32_t p4[4] = {wv[it][c].x, wv[it][c].y, wv[it][c].z, wv[it][c].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = fmaf(__uint_as_float(p4[j] << 16), zc[c][2 * j], acc);
+        acc = fmaf(__uint_as_float(p4[j] & 0xffff0000u), zc[c][2 * j + 1], acc);
+      }
     }
     // reduce over the TPR lanes of the row (TPR divides 64, lanes contiguous)
 #pragma unroll
@@ -198,17 +207,23 @@ hipError_t launch_svd_predict(const sfn_svd& s, const void* x, int32_t* cand, in
   if (e != hipSuccess) return e;
   const int nch = s.r / 8;
   const char* l = static_cast<const char*>(s.l);
+#define SFN_P_LAUNCH(TPR, CH)                                                                                      \
+  hipLaunchKernelGGL((svd_p_kernel<TPR, CH>), dim3(ntiles), dim3(512), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, \
+                     n_cand, p_out, flags, ntiles)
   if (nch <= 8) {
-    hipLaunchKernelGGL((svd_p_kernel<8>), dim3(ntiles), dim3(512), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
+    SFN_P_LAUNCH(8, 1);
   } else if (nch <= 16) {
-    hipLaunchKernelGGL((svd_p_kernel<16>), dim3(ntiles), dim3(512), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
+    SFN_P_LAUNCH(16, 1);
   } else if (nch <= 32) {
-    hipLaunchKernelGGL((svd_p_kernel<32>), dim3(ntiles), dim3(512), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
+    SFN_P_LAUNCH(32, 1);
   } else if (nch <= 64) {
-    hipLaunchKernelGGL((svd_p_kernel<64>), dim3(ntiles), dim3(512), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, n_cand, p_out, flags, ntiles);
+    SFN_P_LAUNCH(64, 1);
+  } else if (nch <= 128) {
+    SFN_P_LAUNCH(64, 2);
   } else {
-    return hipErrorInvalidValue;  // r > 512 needs more than one wave per row
+    return hipErrorInvalidValue;  // r > 1024
   }
+#undef SFN_P_LAUNCH
   return hipGetLastError();
 }
 

@@ -76,6 +76,7 @@ extern "C" {
 #define SFN_MAX_CHUNK 16  /* tokens per ffn_dense_chunk call (the Sirius chunk) */
 #define SFN_MAX_D 16384
 #define SFN_MAX_F 262144
+#define SFN_MAX_RANK 1024 /* SVD predictor rank */
 
 /* One FFN layer. All pointers device, each matrix [f, d] row-major in `wdtype`. */
 typedef struct sfn_ffn {
@@ -91,7 +92,7 @@ typedef struct sfn_ffn {
 
 /* Rank-r SVD predictor of one layer's gate (bf16 factors). All pointers device. */
 typedef struct sfn_svd {
-  int32_t d, f, r;   /* hidden size, neurons, rank (8 <= r <= 512, r % 8 == 0) */
+  int32_t d, f, r;   /* hidden size, neurons, rank (8 <= r <= 1024, r % 8 == 0) */
   int32_t reserved;  /* must be 0 */
   const void* q;     /* [r, d] bf16: V_r^T, the top-r right singular vectors as rows */
   const void* l;     /* [f, r] bf16: U_r diag(sigma_r) */

@@ -46,6 +46,7 @@ from .ffn import (  # noqa: F401
 from .calibrate import calibrate_cats, order_statistic_rank  # noqa: F401
 from .svd import (  # noqa: F401
     svd_factors,
+    svd_factors_whitened,
     svd_predict,
     svd_candidates,
     calibrate_tau,

@@ -35,6 +35,30 @@ def svd_factors(Wg, r):
     return Q, L
 
 
+def svd_factors_whitened(Wg, Xcal, r, ridge=1e-6):
+    """Rank-r predictor of Wg fitted to the inputs it will see (data whitening).
+
+    The pages list data whitening as a step that improves the predictor (Table 3,
+    "+ Data whitening") without a formula. Reading used here: minimize the mean squared
+    prediction error over the calibration tokens, E ||(Wg - L Q) x||^2, which is
+    ||(Wg - L Q) S||_F^2 for the input second moment C = X^T X / n = S S^T (Cholesky;
+    a ridge of `ridge` times the mean diagonal keeps C positive definite). Its minimizer
+    is the truncated SVD of the whitened gate Wg S = U diag(sigma) V^T mapped back:
+    L = U_r diag(sigma_r), Q = V_r^T S^{-1}. With C = I this is svd_factors.
+    """
+    Wg = np.asarray(Wg, dtype=np.float64)
+    X = np.asarray(Xcal, dtype=np.float64)
+    if not (1 <= r <= min(Wg.shape)):
+        raise ValueError("rank r must lie in [1, min(f, d)]")
+    C = X.T @ X / X.shape[0]
+    C = C + ridge * np.trace(C) / C.shape[0] * np.eye(C.shape[0])
+    S = np.linalg.cholesky(C)
+    U, sig, Vt = np.linalg.svd(Wg @ S, full_matrices=False)
+    L = U[:, :r] * sig[None, :r]
+    Q = np.linalg.solve(S.T, Vt[:r, :].T).T  # V_r^T S^{-1}
+    return Q, L
+
+
 def svd_predict(Q, L, x, b=None):
     """Predicted gate p = L (Q x) (+ b) of one token (float64).
 

@@ -306,6 +306,43 @@ def pin_svd_predict_full_rank():
     assert np.allclose(oracle.svd_predict(Q1, L1, x, b), a * (c @ x) + b, atol=1e-12)
 
 
+def pin_svd_whitened_identity():
+    """Tokens whose second moment is exactly the identity (X = sqrt(n) times an
+    orthonormal basis): the whitened predictor is the plain truncated SVD, L Q equal to
+    the rank-r truncation of Wg."""
+    f, d, r, n = 30, 12, 5, 48
+    Wg = np.random.default_rng(20).standard_normal((f, d))
+    X = np.sqrt(n) * _orthonormal(21, n, d)
+    assert np.allclose(X.T @ X / n, np.eye(d), atol=1e-12)
+    Qw, Lw = oracle.svd_factors_whitened(Wg, X, r, ridge=0.0)
+    U, sg, Vt = np.linalg.svd(Wg, full_matrices=False)
+    assert np.allclose(Lw @ Qw, (U[:, :r] * sg[:r]) @ Vt[:r], atol=1e-10)
+
+
+def pin_svd_whitened_optimal():
+    """Anisotropic tokens with a test-chosen covariance C = A A^T: over those tokens the
+    whitened predictor's mean squared error is the tail energy sum_{j>r} s_j^2 of
+    Wg C^{1/2} (any square root: the singular values do not depend on it), no larger
+    than the plain SVD's error, and no rank-r perturbation of it does better."""
+    f, d, r, n = 26, 10, 3, 400
+    g = np.random.default_rng(22)
+    Wg = g.standard_normal((f, d))
+    A = g.standard_normal((d, d)) @ np.diag(np.linspace(0.1, 2.5, d))
+    X = g.standard_normal((n, d)) @ A.T
+    C = X.T @ X / n
+    w, V = np.linalg.eigh(C)
+    root = (V * np.sqrt(w)) @ V.T  # symmetric square root, not the oracle's Cholesky factor
+    tail = (np.linalg.svd(Wg @ root, compute_uv=False)[r:] ** 2).sum()
+    Qw, Lw = oracle.svd_factors_whitened(Wg, X, r, ridge=0.0)
+    mse = lambda M: np.mean(np.sum((X @ (Wg - M).T) ** 2, axis=1))  # noqa: E731
+    assert abs(mse(Lw @ Qw) - tail) <= 1e-9 * tail
+    Qp, Lp = oracle.svd_factors(Wg, r)
+    assert mse(Lw @ Qw) <= mse(Lp @ Qp) * (1 + 1e-12)
+    for k in range(3):
+        dl = g.standard_normal(Lw.shape) * 1e-3
+        assert mse((Lw + dl) @ Qw) > mse(Lw @ Qw)
+
+
 def pin_tau_golden():
     fx = _load("tau_tiny.json")
     P, G = np.array(fx["P"], float), np.array(fx["G"], float)

@@ -73,7 +73,8 @@ def test_workspace_size_queries():
     assert lib.sparse_ffn_workspace_size(ctypes.byref(_ffn(wdtype=7)), 1) == 0
     svd = B.sfn_svd(4096, 11008, 256, 0, FAKE, FAKE, None, FAKE)
     assert lib.svd_predict_workspace_size(ctypes.byref(svd)) > 0
-    assert lib.svd_predict_workspace_size(ctypes.byref(B.sfn_svd(4096, 11008, 1024, 0, FAKE, FAKE, None, FAKE))) == 0
+    assert lib.svd_predict_workspace_size(ctypes.byref(B.sfn_svd(4096, 11008, 1032, 0, FAKE, FAKE, None, FAKE))) == 0
+    assert lib.svd_predict_workspace_size(ctypes.byref(B.sfn_svd(4096, 11008, 1024, 0, FAKE, FAKE, None, FAKE))) > 0
 
 
 @needs_lib

@@ -47,6 +47,28 @@ def _svd_factors_no_sigma(Wg, r):
     return Vt[:r].copy(), U[:, :r].copy()
 
 
+def _whitened_no_back_map(Wg, Xcal, r, ridge=1e-6):
+    """Whitened SVD that forgets to map Q back through S^{-1}."""
+    Wg = np.asarray(Wg, float)
+    X = np.asarray(Xcal, float)
+    C = X.T @ X / X.shape[0]
+    C = C + ridge * np.trace(C) / C.shape[0] * np.eye(C.shape[0])
+    S = np.linalg.cholesky(C)
+    U, sig, Vt = np.linalg.svd(Wg @ S, full_matrices=False)
+    return Vt[:r].copy(), U[:, :r] * sig[None, :r]
+
+
+def _whitened_transposed_root(Wg, Xcal, r, ridge=1e-6):
+    """Whitened SVD with the Cholesky factor on the wrong side (S^T instead of S)."""
+    Wg = np.asarray(Wg, float)
+    X = np.asarray(Xcal, float)
+    C = X.T @ X / X.shape[0]
+    C = C + ridge * np.trace(C) / C.shape[0] * np.eye(C.shape[0])
+    S = np.linalg.cholesky(C).T
+    U, sig, Vt = np.linalg.svd(Wg @ S, full_matrices=False)
+    return np.linalg.solve(S.T, Vt[:r].T).T, U[:, :r] * sig[None, :r]
+
+
 def _tau_swapped(P, G, s):
     return osvd.__dict__["_orig_calibrate_tau"](P, G, 1.0 - s)
 
@@ -72,6 +94,10 @@ MUTATIONS = {
     "rank_off_by_one": [(ocal, "order_statistic_rank", _rank_off_by_one)],
     "svd_sigma_dropped": [(osvd, "svd_factors", _svd_factors_no_sigma), (oracle, "svd_factors", _svd_factors_no_sigma)],
     "tau_classes_swapped": [(oracle, "calibrate_tau", _tau_swapped)],
+    "whitened_no_back_map": [(osvd, "svd_factors_whitened", _whitened_no_back_map),
+                             (oracle, "svd_factors_whitened", _whitened_no_back_map)],
+    "whitened_transposed_root": [(osvd, "svd_factors_whitened", _whitened_transposed_root),
+                                 (oracle, "svd_factors_whitened", _whitened_transposed_root)],
     "down_transposed": [(offn, "dense_ffn", _dense_ffn_transposed), (oracle, "dense_ffn", _dense_ffn_transposed)],
     "bf16_decode_shift": [(offn, "bf16_to_f64", _bf16_wrong_shift), (oracle, "bf16_to_f64", _bf16_wrong_shift)],
 }
