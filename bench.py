@@ -382,76 +382,100 @@ def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4):
     del layers, ws, X, Y
     torch.cuda.empty_cache()
 
-    # ReGLU layers with the rank-256 SVD predictor, sequential pipeline (predict, then the
-    # gate on the candidates and up/down where ReLU(gate) > 0)
+    # ReGLU layers with SVD predictors (factors and thresholds from the offline
+    # preparation): the sequential pipeline with a rank-256 predictor (predict, then the
+    # gate on the candidates and up/down where ReLU(gate) > 0) and the parallel pipeline
+    # with a rank-1024 whitened predictor (predict, then gate, up and down rows of every
+    # candidate in one pass)
+    from contextual_activation_sparsity_amd import prepare
     w3 = inputs.workload(3)
-    d, f, r = w3.d, w3.f, w3.rank
-    preds, layers = [], []
-    xcal = xtok(w3, (w3.n_tau_cal, d), inputs.STREAM_TAU).float()
+    d, f = w3.d, w3.f
+    layers, pred_seq, pred_par = [], [], []
+    # calibration tokens for whitening and thresholds: 2d of them (whitening needs n >= d)
+    xcal = xtok(w3, (max(w3.n_tau_cal, 2 * d), d), inputs.STREAM_TAU)
+    t0 = time.perf_counter()
     for l in range(n_layers):
-        A = torch.randn((f, r), generator=torch.Generator(device=dev).manual_seed(inputs.seed(3, l, inputs.T_A)),
-                        device=dev) / np.sqrt(r)
-        Bm = torch.randn((r, d), generator=torch.Generator(device=dev).manual_seed(inputs.seed(3, l, inputs.T_B)),
-                         device=dev) * w3.w_std
+        A = torch.randn((f, w3.rank), generator=torch.Generator(device=dev).manual_seed(
+            inputs.seed(3, l, inputs.T_A)), device=dev) / np.sqrt(w3.rank)
+        Bm = torch.randn((w3.rank, d), generator=torch.Generator(device=dev).manual_seed(
+            inputs.seed(3, l, inputs.T_B)), device=dev) * w3.w_std
         noise = torch.randn((f, d), generator=torch.Generator(device=dev).manual_seed(
             inputs.seed(3, l, inputs.T_NOISE)), device=dev) * w3.w_std
         wg = (A @ Bm + 0.1 * noise).to(torch.bfloat16)
+        del A, Bm, noise
         bias = (-1.2815516 * wg.float().norm(dim=1)).contiguous()
-        # exact rank-r factors of A B: B^T = Qb Rb, so A B = (A Rb^T) Qb^T
-        Qb, Rb = torch.linalg.qr(Bm.t())
-        q = Qb.t().contiguous().to(torch.bfloat16)
-        lf = (A @ Rb.t()).contiguous().to(torch.bfloat16)
-        # per-neuron thresholds at s: between the mean prediction over calibration tokens
-        # whose gate is inactive and over those where it is active
-        P = (xcal @ q.float().t()) @ lf.float().t() + bias
-        Gt = xcal.bfloat16().float() @ wg.float().t() + bias
-        on = (Gt > 0).float()
-        n_on, n_off = on.sum(0), (1 - on).sum(0)
-        m_on = (P * on).sum(0) / n_on.clamp(min=1)
-        m_off = (P * (1 - on)).sum(0) / n_off.clamp(min=1)
-        tau = ((1 - w3.s) * m_off + w3.s * m_on)
-        tau = torch.where((n_on > 0) & (n_off > 0), tau, torch.zeros_like(tau)).contiguous()
-        del P, Gt, on, A, Bm, noise
+        gates = xcal.float() @ wg.float().t() + bias
+        for preds, r, whiten in ((pred_seq, 256, False), (pred_par, 1024, True)):
+            q, lf = prepare.svd_factors(wg, r, x_cal=xcal if whiten else None)
+            tau = prepare.calibrate_tau(prepare.predictions(q, lf, xcal.float(), bias), gates, w3.s)
+            preds.append(B.SVDPredictor(q, lf, tau, b=bias))
+            torch.cuda.synchronize()
+            log(f"  layer {l}: rank-{r} {'whitened ' if whiten else ''}factors and thresholds at "
+                f"{time.perf_counter() - t0:.1f} s")
+        del gates
         layers.append(B.FFNLayer(wg, gauss((f, d), w3.w_std, inputs.seed(3, l, inputs.T_UP)),
                                  gauss((f, d), w3.w_std, inputs.seed(3, l, inputs.T_DOWN)), b_gate=bias,
                                  act=B.SFN_ACT_RELU))
-        preds.append(B.SVDPredictor(q, lf, tau, b=bias))
-    ws = B.workspace(max(B.sparse_ffn_workspace_size(layers[0], 1), B.svd_predict_workspace_size(preds[0])))
-    wsp_ = B.workspace(B.svd_predict_workspace_size(preds[0]))
+    torch.cuda.synchronize()
+    log(f"  svd factors and thresholds for {n_layers} layers in {time.perf_counter() - t0:.1f} s")
+    ws = B.workspace(B.sparse_ffn_workspace_size(layers[0], 1))
+    wsp_ = B.workspace(max(B.svd_predict_workspace_size(pred_seq[0]), B.svd_predict_workspace_size(pred_par[0])))
     X = xtok(w3, (n_warm + n_steps, n_layers, d), inputs.STREAM_DECODE)
     y = torch.zeros((n_layers, d), dtype=torch.float32, device=dev)
     cand = torch.zeros((n_layers, f), dtype=torch.int32, device=dev)
     ncand = torch.zeros((n_layers, 1), dtype=torch.int32, device=dev)
     nact = torch.zeros((n_layers, 1), dtype=torch.int32, device=dev)
 
-    def svd_calls(tok, l, counts=False):
-        return [(lib.svd_predict, (ctypes.byref(preds[l].c), X[tok, l].data_ptr(), cand[l].data_ptr(),
-                                   ncand[l].data_ptr(), None, wsp_.data_ptr(), wsp_.numel())),
+    def predict(preds, tok, l):
+        return (lib.svd_predict, (ctypes.byref(preds[l].c), X[tok, l].data_ptr(), cand[l].data_ptr(),
+                                  ncand[l].data_ptr(), None, wsp_.data_ptr(), wsp_.numel()))
+
+    def seq_calls(tok, l, counts=False):
+        return [predict(pred_seq, tok, l),
                 (lib.sparse_ffn_decode, (ctypes.byref(layers[l].c), X[tok, l].data_ptr(), 1, None,
                                          cand[l].data_ptr(), ncand[l].data_ptr(), None, y[l].data_ptr(), None,
                                          nact[l].data_ptr() if counts else None, ws.data_ptr(), ws.numel()))]
-    dc, da = [], []
+
+    def par_calls(tok, l):
+        return [predict(pred_par, tok, l),
+                (lib.sparse_ffn_decode_parallel, (ctypes.byref(layers[l].c), X[tok, l].data_ptr(), cand[l].data_ptr(),
+                                                  ncand[l].data_ptr(), y[l].data_ptr(), ws.data_ptr(), ws.numel()))]
+
+    def leg(calls):
+        steps = [[c for l in range(n_layers) for c in calls(tok, l)] for tok in range(n_warm, n_warm + n_steps)]
+        time_mixed(torch, [[c for l in range(n_layers) for c in calls(tok, l)] for tok in range(n_warm)], mode)
+        return time_mixed(torch, steps, mode) * 1e3 / (n_steps * n_layers)
+
+    # densities: untimed passes over the timed tokens
+    dc, da, dcp = [], [], []
     for tok in range(n_warm, n_warm + n_steps):
         for l in range(n_layers):
-            for fn, a in svd_calls(tok, l, True):
+            for fn, a in seq_calls(tok, l, True):
                 fn(*a, torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
         dc.append(ncand.float().mean().item())
         da.append(nact.float().mean().item())
-    nc, na = float(np.mean(dc)), float(np.mean(da))
-    time_mixed(torch, [[c for l in range(n_layers) for c in svd_calls(tok, l)] for tok in range(n_warm)], mode)
-    ms = time_mixed(torch, [[c for l in range(n_layers) for c in svd_calls(tok, l)]
-                            for tok in range(n_warm, n_warm + n_steps)], mode)
-    us = ms * 1e3 / (n_steps * n_layers)
-    pred_only = time_mixed(torch, [[svd_calls(tok, l)[0] for l in range(n_layers)]
-                                   for tok in range(n_warm, n_warm + n_steps)], mode) * 1e3 / (n_steps * n_layers)
-    byts = 2.0 * r * (d + f) + 8.0 * f + 2.0 * nc * d + 4.0 * na * d + 6.0 * d
-    out["reglu_svd_r256_s50"] = {"d": d, "f": f, "r": r, "s": w3.s, "layers_timed": n_layers,
-                                 "us_per_layer": us, "predictor_us": pred_only,
-                                 "candidate_density": nc / f, "active_density": na / f,
-                                 "algorithmic_bytes_per_layer": byts, "gbs": byts / (us * 1e-6) / 1e9,
-                                 "tokens_per_s_32_layers": 1.0 / (32 * us * 1e-6)}
-    log(f"  extra svd: {us:.2f} us/layer (predictor {pred_only:.2f}), cand {nc / f:.3f}, active {na / f:.3f}")
+        for l in range(n_layers):
+            fn, a = predict(pred_par, tok, l)
+            fn(*a, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        dcp.append(ncand.float().mean().item())
+    nc, na, ncp = float(np.mean(dc)), float(np.mean(da)), float(np.mean(dcp))
+    for name, r, calls, byts in (
+            ("reglu_svd_r256_s50", 256, seq_calls, 2.0 * 256 * (d + f) + 8.0 * f + 2.0 * nc * d + 4.0 * na * d + 6.0 * d),
+            ("reglu_svd_r1024_whitened_parallel", 1024, par_calls,
+             2.0 * 1024 * (d + f) + 8.0 * f + 6.0 * ncp * d + 6.0 * d)):
+        us = leg(calls)
+        preds = pred_seq if r == 256 else pred_par
+        pred_us = time_mixed(torch, [[predict(preds, tok, l) for l in range(n_layers)]
+                                     for tok in range(n_warm, n_warm + n_steps)], mode) * 1e3 / (n_steps * n_layers)
+        out[name] = {"d": d, "f": f, "r": r, "s": w3.s, "layers_timed": n_layers, "us_per_layer": us,
+                     "predictor_us": pred_us, "candidate_density": (nc if r == 256 else ncp) / f,
+                     "algorithmic_bytes_per_layer": byts, "gbs": byts / (us * 1e-6) / 1e9,
+                     "tokens_per_s_32_layers": 1.0 / (32 * us * 1e-6)}
+        if r == 256:
+            out[name]["active_density"] = na / f
+        log(f"  extra {name}: {us:.2f} us/layer (predictor {pred_us:.2f}), cand {out[name]['candidate_density']:.3f}")
     return out
 
 

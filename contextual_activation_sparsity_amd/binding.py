@@ -37,6 +37,7 @@ EXPORTED = (
     "sparse_ffn_strerror",
     "sparse_ffn_calibrate",
     "sparse_ffn_decode",
+    "sparse_ffn_decode_parallel",
     "svd_predict",
     "ffn_dense_chunk",
 )
@@ -68,6 +69,8 @@ _lib.sparse_ffn_calibrate.argtypes = [ctypes.POINTER(sfn_ffn), _vp, _i32, _f32, 
 _lib.sparse_ffn_calibrate.restype = ctypes.c_int
 _lib.sparse_ffn_decode.argtypes = [ctypes.POINTER(sfn_ffn), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.sparse_ffn_decode.restype = ctypes.c_int
+_lib.sparse_ffn_decode_parallel.argtypes = [ctypes.POINTER(sfn_ffn), _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.sparse_ffn_decode_parallel.restype = ctypes.c_int
 _lib.svd_predict.argtypes = [ctypes.POINTER(sfn_svd), _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.svd_predict.restype = ctypes.c_int
 _lib.ffn_dense_chunk.argtypes = [ctypes.POINTER(sfn_ffn), _vp, _i32, _vp, _vp, _sz, _vp]
@@ -201,6 +204,15 @@ def sparse_ffn_decode(layer: FFNLayer, x: torch.Tensor, t: Optional[torch.Tensor
         _ptr(active_idx, "active_idx", torch.int32, B * layer.f), _ptr(n_active, "n_active", torch.int32, B),
         _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "sparse_ffn_decode")
+
+
+def sparse_ffn_decode_parallel(layer: FFNLayer, x: torch.Tensor, cand: torch.Tensor, n_cand: torch.Tensor,
+                               ws: torch.Tensor, y: torch.Tensor, stream=None):
+    st = _lib.sparse_ffn_decode_parallel(
+        ctypes.byref(layer.c), _ptr(x, "x", layer.dtype, layer.d), _ptr(cand, "cand", torch.int32),
+        _ptr(n_cand, "n_cand", torch.int32, 1), _ptr(y, "y", torch.float32, layer.d), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "sparse_ffn_decode_parallel")
 
 
 def svd_predict(pred: SVDPredictor, x: torch.Tensor, cand_idx: torch.Tensor, n_cand: torch.Tensor,

@@ -144,6 +144,42 @@ int sparse_ffn_decode(const sfn_ffn* ffn, const void* x, int32_t B, const float*
   }
 }
 
+int sparse_ffn_decode_parallel(const sfn_ffn* ffn, const void* x, const int32_t* cand, const int32_t* n_cand,
+                               float* y, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    int st = check_ffn(ffn, true);
+    if (st != SFN_OK) return st;
+    if (!x || !cand || !n_cand || !y) return SFN_EINVAL;
+    if (!aligned16(x) || !aligned16(y)) return SFN_EALIGN;
+    if (reinterpret_cast<uintptr_t>(cand) & 3u) return SFN_EALIGN;
+    const int wb = wbytes(ffn->wdtype);
+    st = check_ws(ws, ws_bytes, sfn::decode_workspace_bytes(ffn->d, ffn->f, wb, 1));
+    if (st != SFN_OK) return st;
+
+    sfn::DecodeArgs a{};
+    a.wg = static_cast<const char*>(ffn->w_gate);
+    a.wu = static_cast<const char*>(ffn->w_up);
+    a.wd = static_cast<const char*>(ffn->w_down_t);
+    a.bias = ffn->b_gate;
+    a.x = static_cast<const char*>(x);
+    a.cand = cand;
+    a.n_cand = n_cand;
+    a.y = y;
+    a.d = ffn->d;
+    a.f = ffn->f;
+    a.nch = ffn->d * wb / 16;
+    a.row_bytes = ffn->d * wb;
+    a.nb = 1;
+    a.act = ffn->act;
+    a.G = sfn::decode_grid(ffn->f);
+    a.n_red = sfn::decode_reducers(a.G, 1, ffn->d);
+    sfn::decode_carve(a, ws, wb);
+    return hip_status(sfn::launch_decode_parallel(a, ffn->wdtype, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return SFN_EHIP;
+  }
+}
+
 int sparse_ffn_calibrate(const sfn_ffn* ffn, const void* x_cal, int32_t n, float k, float* t_out,
                          float* scores_out, void* ws, size_t ws_bytes, void* stream) {
   try {

@@ -534,6 +534,150 @@ struct UpDownKernel {
   }
 };
 
+// ------------------------------------------------------------ parallel-pipeline kernel
+// Candidate rows in one pass ("SVD Contextual Sparsity Predictors for Fast LLM
+// Inference", Table 2: the parallel pipeline): for the rows of a candidate list the gate,
+// up and down rows are read in the same step, and y = sum over the candidates of
+// act(g_i + b_i) u_i Dt[i, :]. Each of the G workgroups takes an equal share of the
+// list; one token. With ReLU the result is that of the sequential pipeline (the gate
+// zeroes the rest); it reads all three rows of every candidate but needs no gate pass.
+template <int WT, int CPT, int TPR, int R>
+struct ParKernel {
+  using S = Shape<WT, 1, CPT, TPR, R>;
+  using CK = typename S::CK;
+  static constexpr int RPG = S::RPG, RG = S::RG, KV = S::KV;
+  static constexpr int V2 = 2 * R;  // gate and up of the step's rows
+  static_assert(RG <= 64, "one lane of wave 0 per row of a step");
+
+  struct Smem {
+    int qrow[kTMax];
+    float qb[kTMax];
+    float wpart[kNW][V2];
+    float h[64];
+  };
+
+  // Loads of one step: Wg, Wu and Dt rows of share entries [base, base + n), or (step
+  // none) all from x, L1-resident, results unused.
+  __device__ __forceinline__ static void issue(const DevArgs& a, const Smem& sm, const StepDesc& sd, int nq, int rl,
+                                               int cl, uint4 (&wg)[R][CPT], uint4 (&wu)[R][CPT],
+                                               uint4 (&wd)[R][CPT]) {
+    const bool live = sd.kind == STEP_UPDOWN;
+    const SFN_GLOBAL char* pg = live ? a.wg : a.x;
+    const SFN_GLOBAL char* pu = live ? a.wu : a.x;
+    const SFN_GLOBAL char* pd = live ? a.wd : a.x;
+    const size_t rb = live ? (size_t)a.row_bytes : 0;
+    const int jmax = nq > 0 ? nq - 1 : 0;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int j = min(sd.base + rl + RPG * k, jmax);
+      const size_t ro = (size_t)sm.qrow[j] * rb;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        int ch = cl + TPR * c;
+        ch = ch < a.nch ? ch : 0;
+        wg[k][c] = ldg16(pg + ro + (size_t)ch * 16);
+        wu[k][c] = ldg16(pu + ro + (size_t)ch * 16);
+        wd[k][c] = ldg16(pd + ro + (size_t)ch * 16);
+      }
+    }
+  }
+
+  __device__ static void run(const DecodeArgs& args) {
+    const DevArgs a = dev_args(args);
+    __shared__ Smem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rl = tid / TPR, cl = tid % TPR;
+    const int w = blockIdx.x;
+    const int n = min(max(*a.n_cand, 0), a.f);  // a count beyond f cannot be a valid list
+    const int s0 = share_begin(w, n, a.G);
+    const int nq = share_begin(w + 1, n, a.G) - s0;
+    for (int j = tid; j < nq; j += kNT) {
+      const int row = min(max(a.cand[s0 + j], 0), a.f - 1);  // in bounds
+      sm.qrow[j] = row;
+      sm.qb[j] = a.bias ? a.bias[row] : 0.f;
+    }
+    float acc[CPT][KV];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int v = 0; v < KV; ++v) acc[c][v] = 0.f;
+    uint4 xr[1][CPT];
+    S::load_x(a, cl, xr);
+    __syncthreads();
+
+    auto process = [&](const StepDesc& sd, const uint4 (&wg)[R][CPT], const uint4 (&wu)[R][CPT],
+                       const uint4 (&wd)[R][CPT]) {
+      float s[V2];
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        float dg = 0.f, du = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          dg = CK::dot(wg[k][c], xr[0][c], dg);
+          du = CK::dot(wu[k][c], xr[0][c], du);
+        }
+        s[k] = dg;
+        s[R + k] = du;
+      }
+      S::template reduce_to_lds<V2>(sm.wpart, s);
+      __syncthreads();
+      if (wave == 0 && lane < sd.n) {
+        const int j = sd.base + lane;
+        const int rlj = lane % RPG, k = lane / RPG;
+        const float g = S::template wave_partial_sum<V2>(sm.wpart, rlj, k) + sm.qb[j];
+        const float u = S::template wave_partial_sum<V2>(sm.wpart, rlj, R + k);
+        sm.h[lane] = (a.act == 0 ? silu_f(g) : fmaxf(g, 0.f)) * u;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int jj = rl + RPG * k;
+        if (jj < sd.n) {
+          const float hv = sm.h[jj];
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) CK::axpy(hv, wd[k][c], acc[c]);
+        }
+      }
+    };
+
+    const int nstep = (nq + RG - 1) / RG;
+    uint4 ag[R][CPT], au[R][CPT], ad[R][CPT], bg[R][CPT], bu[R][CPT], bd[R][CPT];
+    auto step = [&](int st) -> StepDesc {
+      StepDesc sd{STEP_NONE, 0, 0};
+      if (st < nstep) {
+        sd.kind = STEP_UPDOWN;
+        sd.base = st * RG;
+        sd.n = min(RG, nq - sd.base);
+      }
+      return sd;
+    };
+    StepDesc sa = step(0);
+    issue(a, sm, sa, nq, rl, cl, ag, au, ad);
+    for (int st = 0; st < nstep; st += 2) {
+      const StepDesc sb = step(st + 1);
+      issue(a, sm, sb, nq, rl, cl, bg, bu, bd);
+      process(sa, ag, au, ad);
+      if (st + 1 >= nstep) break;
+      sa = step(st + 2);
+      issue(a, sm, sa, nq, rl, cl, ag, au, ad);
+      process(sb, bg, bu, bd);
+    }
+
+    // ---- partial of y (read by the reduce kernel after this launch completes)
+    SFN_GLOBAL float* prow = a.part + (size_t)(w * RPG + rl) * a.d;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = cl + TPR * c;
+      if (ch < a.nch) {
+        SFN_GLOBAL float* dst = prow + (size_t)ch * KV;
+#pragma unroll
+        for (int v = 0; v < KV; v += 4)
+          *reinterpret_cast<SFN_GLOBAL f32x4_t*>(dst + v) = f32x4_t{acc[c][v], acc[c][v + 1], acc[c][v + 2], acc[c][v + 3]};
+      }
+    }
+  }
+};
+
 // ---------------------------------------------------------------------- reduce kernel
 // y = sum of the partials of the up/down kernel, in chunks of 32 columns (128 bytes of
 // each partial row): lane l of group g sums column l of partials g, g + 16, g + 32, ...
@@ -661,6 +805,30 @@ hipError_t launch_pair(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int WT, int CPT, int TPR, int R>
+__global__ __launch_bounds__(kNT) void decode_parallel_kernel(DecodeArgs a) {
+  ParKernel<WT, CPT, TPR, R>::run(a);
+}
+
+template <int WT, int CPT, int TPR, int R>
+hipError_t launch_parallel(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((decode_parallel_kernel<WT, CPT, TPR, R>), dim3(a.G), dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.n_red), dim3(ReduceKernel::kRT), 0, s, a, a.G * (kNT / TPR));
+  return hipGetLastError();
+}
+
+template <int WT>
+hipError_t dispatch_parallel(const DecodeArgs& a, hipStream_t s) {
+  // three rows per step entry: 12 weight loads in flight per thread and buffer
+  if (a.nch > 2048) return hipErrorInvalidValue;
+  if (a.nch > 1024) return launch_parallel<WT, 4, 512, 1>(a, s);
+  if (a.nch > 512) return launch_parallel<WT, 2, 512, 2>(a, s);
+  if (a.nch > 256) return launch_parallel<WT, 1, 512, 4>(a, s);
+  if (a.nch > 128) return launch_parallel<WT, 1, 256, 4>(a, s);
+  if (a.nch > 64) return launch_parallel<WT, 1, 128, 4>(a, s);
+  return launch_parallel<WT, 1, 64, 2>(a, s);
+}
+
 template <int WT, int BMAX>
 hipError_t dispatch_tpr(const DecodeArgs& a, hipStream_t s) {
   // rows per thread per half step: 16 weight loads in flight per thread and buffer for
@@ -731,6 +899,11 @@ void decode_carve(DecodeArgs& a, void* ws, int wb) {
   a.sel_bits = reinterpret_cast<uint8_t*>(p + off);
   off = align256(off + (size_t)a.f);
   a.part = reinterpret_cast<float*>(p + off);
+}
+
+hipError_t launch_decode_parallel(const DecodeArgs& a, int wdtype, hipStream_t s) {
+  if (a.G > kGMax) return hipErrorInvalidValue;
+  return wdtype == WT_BF16 ? dispatch_parallel<WT_BF16>(a, s) : dispatch_parallel<WT_F32>(a, s);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int wdtype, hipStream_t s) {

@@ -50,6 +50,8 @@ int decode_rows_side_by_side(int nch);
 size_t decode_workspace_bytes(int d, int f, int wb, int nb);
 void decode_carve(DecodeArgs& a, void* ws, int wb);
 hipError_t launch_decode(const DecodeArgs& a, int wdtype, hipStream_t stream);
+// Candidate rows in one pass (gate, up and down rows together), then the reduce kernel.
+hipError_t launch_decode_parallel(const DecodeArgs& a, int wdtype, hipStream_t stream);
 
 size_t chunk_workspace_bytes(int d, int f, int wdtype, int n);
 hipError_t launch_dense_chunk(const sfn_ffn& ffn, const void* x, int n, float* y, void* ws, hipStream_t stream);

@@ -25,6 +25,7 @@ def svd_factors(w_gate: torch.Tensor, r: int, x_cal: Optional[torch.Tensor] = No
     [n, d] (data whitening): the factors minimize the mean squared prediction error over
     those tokens. With the second moment C = x^T x / n = S S^T (Cholesky, plus a small
     ridge), take the truncated SVD of w_gate S and map it back: q = V_r^T S^{-1}.
+    Whitening needs at least d calibration tokens.
     """
     wd = _work_dtype(w_gate)
     W = w_gate.to(wd)
@@ -35,6 +36,10 @@ def svd_factors(w_gate: torch.Tensor, r: int, x_cal: Optional[torch.Tensor] = No
         q = Vh[:r]
     else:
         X = x_cal.to(device=W.device, dtype=wd)
+        if X.ndim != 2 or X.shape[1] != W.shape[1] or X.shape[0] < X.shape[1]:
+            # with fewer tokens than d the second moment is singular: the ridge alone then
+            # decides the factors, and in fp32 the Cholesky factorization can fail
+            raise ValueError("whitening needs calibration tokens x_cal [n, d] with n >= d")
         C = X.T @ X / X.shape[0]
         C = C + ridge * torch.trace(C) / C.shape[0] * torch.eye(C.shape[0], dtype=wd, device=W.device)
         S = torch.linalg.cholesky(C)

@@ -148,6 +148,24 @@ int sparse_ffn_decode(const sfn_ffn* ffn, const void* x, int32_t B, const float*
                       size_t ws_bytes, void* stream);
 
 /*
+ * Candidate rows in one pass for one token: the SVD predictor's parallel pipeline ("SVD
+ * Contextual Sparsity Predictors for Fast LLM Inference", Table 2: parallel pipeline,
+ * against the sequential one of sparse_ffn_decode's candidate mode). For the rows in the
+ * candidate list the gate, up and down rows are read together:
+ *   y = sum over i in cand of act(g_i) u_i Dt[i, :],   g = Wg x + b,  u = Wu x
+ * accumulated in fp32. With ReLU this is the candidate mode's result (the gate zeroes
+ * the rest), reading all three rows of every candidate but with no separate gate pass.
+ *   x      [d] in ffn->wdtype
+ *   cand   candidate rows (device int32; entries are clamped into [0, f)), n_cand its
+ *          device count (clamped into [0, f]); any order, each row at most once
+ *   y      [d] fp32 (device), written
+ * Workspace: as sparse_ffn_decode for one token.
+ */
+int sparse_ffn_decode_parallel(const sfn_ffn* ffn, const void* x, const int32_t* cand,
+                               const int32_t* n_cand, float* y, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
  * SVD predictor for one token ("SVD Contextual Sparsity Predictors for Fast LLM
  * Inference", abstract and Figures 1-3): z = Q x (fp32), p = L z + b, candidates
  * {i : p_i > tau_i} written in ascending order.

@@ -138,4 +138,14 @@ def test_other_calls_validation():
     assert pred(ws_bytes=sneed - 1) == B.SFN_EWORKSPACE
     assert pred(s=B.sfn_svd(4096, 11008, 252, 0, FAKE, FAKE, None, FAKE)) == B.SFN_EALIGN
     assert pred(s=B.sfn_svd(4096, 11008, 256, 1, FAKE, FAKE, None, FAKE)) == B.SFN_EINVAL
+    par = lambda f=ffn, **kw: lib.sparse_ffn_decode_parallel(  # noqa: E731
+        ctypes.byref(f), kw.get("x", FAKE), kw.get("cand", FAKE), kw.get("n", FAKE), kw.get("y", FAKE),
+        kw.get("ws", FAKE), kw.get("ws_bytes", need), None)
+    assert par(cand=None) == B.SFN_EINVAL
+    assert par(n=None) == B.SFN_EINVAL
+    assert par(y=None) == B.SFN_EINVAL
+    assert par(x=FAKE + 4) == B.SFN_EALIGN
+    assert par(cand=FAKE + 2) == B.SFN_EALIGN
+    assert par(ws=None) == B.SFN_EWORKSPACE
+    assert par(ws_bytes=2048) == B.SFN_EWORKSPACE
     assert pred(s=B.sfn_svd(4096, 11008, 256, 0, FAKE, FAKE, None, None)) == B.SFN_EINVAL

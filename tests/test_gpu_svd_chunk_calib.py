@@ -55,7 +55,8 @@ def _svd_case(d, f, r, s, n_tok, n_cal=256, rank_struct=256):
     return raw, pred, ws, (Q64, L64, b, tau), np.array(dens)
 
 
-@pytest.mark.parametrize("d,f,r", [(512, 1000, 64), (1024, 3000, 128), (2048, 700, 352), (4096, 11008, 256)])
+@pytest.mark.parametrize("d,f,r", [(512, 1000, 64), (1024, 3000, 128), (2048, 700, 352), (4096, 11008, 256),
+                                   (1024, 3000, 520), (4096, 11008, 1024)])
 def test_svd_predict(d, f, r):
     _svd_case(d, f, r, 0.5, 3)
 
@@ -90,6 +91,69 @@ def test_svd_sequential_pipeline_end_to_end():
         _, _, y_own = oracle.reglu_sequential(Wg, Wu, Dt, xs[j], act_gpu, b)
         assert normwise_err(y.cpu().numpy()[0], y_own) <= TOL_BF16
         say(f"    candidates {cm.mean():.3f} active {act_gpu.mean():.3f}")
+
+
+def test_svd_parallel_pipeline_end_to_end():
+    """svd_predict -> sparse_ffn_decode_parallel (ReLU): the oracle's result on the same
+    candidates, and the sequential candidate mode's result, within the bf16 tolerance."""
+    d, f, r = 4096, 11008, 256
+    raw, pred, ws_p, (Q64, L64, b, tau), dens = _svd_case(d, f, r, 0.5, 1)
+    Wg, Wu, Dt = (to_f64(raw[k], "bf16") for k in ("w_gate", "w_up", "w_down_t"))
+    layer = B.FFNLayer(to_dev(raw["w_gate"], "bf16"), to_dev(raw["w_up"], "bf16"), to_dev(raw["w_down_t"], "bf16"),
+                       b_gate=torch.from_numpy(raw["b_gate"]).cuda(), act=B.SFN_ACT_RELU)
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, 1))
+    w = inputs.workload(3)
+    xs_raw = inputs.tokens(w, 2, inputs.STREAM_DECODE, d=d)
+    xs = to_f64(xs_raw, "bf16")
+    for j in range(2):
+        say(f"[svd+parallel] token {j}")
+        xd = to_dev(xs_raw[j:j + 1], "bf16")
+        cand = torch.empty(f, dtype=torch.int32, device="cuda")
+        n_cand = torch.empty(1, dtype=torch.int32, device="cuda")
+        B.svd_predict(pred, xd, cand, n_cand, ws_p)
+        y = torch.full((d,), float("nan"), dtype=torch.float32, device="cuda")
+        B.sparse_ffn_decode_parallel(layer, xd, cand, n_cand, ws, y)
+        ys = torch.empty((1, d), dtype=torch.float32, device="cuda")
+        B.sparse_ffn_decode(layer, xd, None, ws, y=ys, cand=cand, n_cand=n_cand)
+        torch.cuda.synchronize()
+        cm = mask_from_idx(cand.cpu().numpy(), int(n_cand.item()), f)
+        _, _, y_ref = oracle.reglu_sequential(Wg, Wu, Dt, xs[j], cm, b)
+        assert normwise_err(y.cpu().numpy(), y_ref) <= TOL_BF16
+        assert normwise_err(y.cpu().numpy(), ys.cpu().numpy()[0]) <= TOL_BF16
+
+
+@pytest.mark.parametrize("wi,d,f,act,frac", [(1, 4096, 11008, "silu", 0.3), (1, 1024, 3000, "relu", 0.5),
+                                              (1, 8192, 2048, "silu", 0.2), (0, 256, 688, "silu", 0.4),
+                                              (1, 2048, 700, "relu", 0.0)])
+def test_parallel_candidate_lists(wi, d, f, act, frac):
+    """Unsorted candidate lists of a given fraction of the rows (empty at 0): y is the
+    FFN masked to those rows, act(g) u summed against Dt, as the oracle computes it."""
+    w = inputs.workload(wi)
+    say(f"[parallel] workload={wi} d={d} f={f} act={act} frac={frac}")
+    raw, dev, host = swiglu_layer_dev(w, 0, d=d, f=f)
+    bias = (np.random.default_rng(5).standard_normal(f) * 0.3).astype(np.float32)
+    layer = B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"], b_gate=torch.from_numpy(bias).cuda(),
+                       act=B.SFN_ACT_SILU if act == "silu" else B.SFN_ACT_RELU)
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, 1))
+    xs_raw = inputs.tokens(w, 2, inputs.STREAM_DECODE, d=d)
+    xs = to_f64(xs_raw, w.dtype)
+    g = np.random.default_rng(6)
+    for j in range(2):
+        rows = g.permutation(f)[: int(frac * f)].astype(np.int32)
+        cand = torch.from_numpy(np.concatenate([rows, np.zeros(f - rows.size, np.int32)])).cuda()
+        n_cand = torch.tensor([rows.size], dtype=torch.int32, device="cuda")
+        y = torch.full((d,), float("nan"), dtype=torch.float32, device="cuda")
+        B.sparse_ffn_decode_parallel(layer, to_dev(xs_raw[j], w.dtype), cand, n_cand, ws, y)
+        torch.cuda.synchronize()
+        mask = np.zeros(f, bool)
+        mask[rows] = True
+        y_ref = oracle.masked_ffn(host["w_gate"], host["w_up"], host["w_down_t"], xs[j], mask, act,
+                                  bias.astype(np.float64))
+        yg = y.cpu().numpy()
+        if rows.size == 0:
+            assert np.all(yg == 0.0)
+        else:
+            assert normwise_err(yg, y_ref) <= (TOL_BF16 if w.dtype == "bf16" else TOL_F32)
 
 
 # ---------------------------------------------------------------------------- chunk

@@ -55,3 +55,13 @@ def test_tau_matches_oracle():
         to = oracle.calibrate_tau(P, G, s)
         assert np.allclose(t, to.astype(np.float32), rtol=1e-6, atol=1e-7)
         assert t[7] == 0.0
+
+
+def test_whitening_rejects_too_few_tokens():
+    Wg, X = _case(5)
+    import pytest
+    for bad in (X[:Wg.shape[1] - 1], X[:, :-1], X[0]):
+        with pytest.raises(ValueError):
+            prepare.svd_factors(torch.from_numpy(Wg), 4, x_cal=torch.from_numpy(bad))
+    with pytest.raises(ValueError):
+        prepare.svd_factors(torch.from_numpy(Wg), Wg.shape[1] + 1)
