@@ -72,6 +72,8 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other workloads (batch 4, SVD pipeline, 70B-shape decode and 16-token chunk)")
+    ap.add_argument("--no-table4", action="store_true",
+                    help="skip the fixed-sparsity protocol (random candidate subsets on every layer, three shapes)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before the stack, copy a MIB-MiB buffer three times (counter scaling)")
     ap.add_argument("--summarize-trace", metavar="DIR")
@@ -637,6 +639,11 @@ def main():
         log("timing the other workloads")
         extra = extras(B, inputs, torch, args.mode)
 
+    t4 = None
+    if not args.no_table4:
+        log("fixed-sparsity protocol (predictor excluded)")
+        t4 = table4(B, inputs, torch, args.mode)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -655,9 +662,69 @@ def main():
         "dense_path": dense,
         "sweep": result_sweep,
         "extras": extra,
+        "table4": t4,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def table4(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4,
+           shapes=((1, 4096, 11008), (2, 4096, 14336), (5, 3584, 18944)), sparsities=(0.2, 0.5, 0.8, 0.95)):
+    """The fixed-sparsity protocol of "SVD Contextual Sparsity Predictors for Fast LLM
+    Inference", Table 4: the same sparsity on every layer and on every projection, the
+    gate included, predictor excluded. Each token and layer gets its own uniformly drawn
+    neuron subset of size round((1 - s) f), ascending, run through the one-pass
+    candidate path (sparse_ffn_decode_parallel, SiLU); the dense FFN is ffn_dense_chunk
+    with one token on the same layers. Reported per shape and sparsity: time per layer,
+    algorithmic bytes and rate, and the FFN speedup over the dense call."""
+    lib = B.raw()
+    dev = "cuda"
+    rows = []
+    for wi, d, f in shapes:
+        w = inputs.workload(wi)
+        layers = [B.FFNLayer(*(inputs.torch_gaussian_bf16((f, d), w.w_std, inputs.seed(wi, l, tid), dev)
+                               for tid in (inputs.T_GATE, inputs.T_UP, inputs.T_DOWN))) for l in range(n_layers)]
+        ws = B.workspace(B.sparse_ffn_workspace_size(layers[0], 16))
+        wsp, wsb = ws.data_ptr(), ws.numel()
+        g = torch.Generator(device=dev)
+        g.manual_seed(1_000_000 * wi + inputs.STREAM_DECODE)
+        X = torch.randn((n_warm + n_steps, n_layers, d), generator=g, device=dev).to(torch.bfloat16)
+        y = torch.zeros((n_layers, d), dtype=torch.float32, device=dev)
+
+        def dense(tok, l):
+            return (lib.ffn_dense_chunk, (ctypes.byref(layers[l].c), X[tok, l].data_ptr(), 1, y[l].data_ptr(),
+                                          wsp, wsb))
+        time_mixed(torch, [[dense(tok, l) for l in range(n_layers)] for tok in range(n_warm)], mode)
+        dense_us = time_mixed(torch, [[dense(tok, l) for l in range(n_layers)]
+                                      for tok in range(n_warm, n_warm + n_steps)], mode) * 1e3 / (n_steps * n_layers)
+        for s in sparsities:
+            n = int(round((1.0 - s) * f))
+            gm = torch.Generator(device=dev)
+            gm.manual_seed(1_000_000 * wi + inputs.STREAM_MASK + int(round(1000 * s)))
+            cand = torch.stack([torch.sort(torch.randperm(f, generator=gm, device=dev)[:n])[0]
+                                for _ in range((n_warm + n_steps) * n_layers)]).to(torch.int32)
+            cand = cand.view(n_warm + n_steps, n_layers, n).contiguous()
+            ncand = torch.full((1,), n, dtype=torch.int32, device=dev)
+
+            def par(tok, l):
+                return (lib.sparse_ffn_decode_parallel, (ctypes.byref(layers[l].c), X[tok, l].data_ptr(),
+                                                         cand[tok, l].data_ptr(), ncand.data_ptr(), y[l].data_ptr(),
+                                                         wsp, wsb))
+            time_mixed(torch, [[par(tok, l) for l in range(n_layers)] for tok in range(n_warm)], mode)
+            us = time_mixed(torch, [[par(tok, l) for l in range(n_layers)]
+                                    for tok in range(n_warm, n_warm + n_steps)], mode) * 1e3 / (n_steps * n_layers)
+            byts = 6.0 * n * d + 4.0 * n + 2.0 * d + 4.0 * d
+            rows.append({"d": d, "f": f, "sparsity": s, "rows": n, "us_per_layer": us, "dense_us_per_layer": dense_us,
+                         "ffn_speedup": dense_us / us, "bytes_ratio": (6.0 * f * d) / byts,
+                         "algorithmic_bytes": byts, "gbs": byts / (us * 1e-6) / 1e9})
+            log(f"  d {d} f {f} sparsity {s}: {us:.2f} us/layer ({rows[-1]['gbs']:.0f} GB/s), dense {dense_us:.2f}, "
+                f"speedup {dense_us / us:.2f}")
+            del cand
+        del layers, ws, X, y
+        torch.cuda.empty_cache()
+    return {"protocol": "fixed sparsity on every layer and projection (gate included), uniformly drawn neuron "
+                        "subsets per token and layer, predictor excluded; one-pass candidate path vs dense FFN call",
+            "layers_timed": n_layers, "steps": n_steps, "rows": rows}
 
 
 def write_traffic(dirs, probe, command):

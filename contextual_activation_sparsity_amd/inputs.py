@@ -62,6 +62,10 @@ WORKLOADS = (
              act="relu", rank=256, s=0.5, n_tau_cal=1024),
     Workload(4, "llama3_70b_ffn_d8192_f28672_bf16_l8", 8192, 28672, 8, "bf16", 0.02,
              sparsities=(0.5,), chunk=16),
+    # SparseQwen2-7B FFN shape, for the fixed-sparsity protocol of SVDP Table 4 (random
+    # neuron subsets at a fixed density on every layer, the gate included)
+    Workload(5, "qwen2_7b_ffn_d3584_f18944_bf16", 3584, 18944, 28, "bf16", 0.02,
+             sparsities=(0.2, 0.5, 0.8, 0.95)),
 )
 
 

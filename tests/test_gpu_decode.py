@@ -118,6 +118,13 @@ def test_llama3_70b_layer():
     _case(w, w.d, w.f, 0.5, 2)
 
 
+def test_qwen2_7b_layer():
+    """SparseQwen2-7B FFN shape: d 3584 is 448 16-byte chunks, not a power of two, so
+    part of each row's threads hold no chunk."""
+    w = inputs.workload(5)
+    _case(w, w.d, w.f, 0.5, 2)
+
+
 def test_batch4_union_llama3_8b_layer():
     w = inputs.workload(2)
     layer, ws, dev, host, t = _case(w, w.d, w.f, 0.5, 8, batch=4)
