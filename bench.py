@@ -384,6 +384,68 @@ def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4):
     del layers, ws, X, Y
     torch.cuda.empty_cache()
 
+    # Sirius correction period at the Llama-3-70B shape over an 8-layer group: 16 sparse
+    # CATS steps (each token through the 8 layers), then the dense verification of the
+    # same 16 tokens per layer, captured together and replayed; against full-model
+    # decoding (16 one-token dense calls per layer)
+    P, nlg = 16, w4.layers
+    layers = swiglu_layers(w4, w4.d, w4.f, nlg)
+    ws = B.workspace(max(B.sparse_ffn_workspace_size(layers[0], w4.n_cal), B.sparse_ffn_workspace_size(layers[0], P)))
+    t = calibrate(layers, w4, 0.5, ws)
+    n_per = 4  # one warm-up period, three timed
+    X = xtok(w4, (n_per, nlg, P, w4.d), inputs.STREAM_DECODE)
+    Ys = torch.zeros((nlg, P, w4.d), dtype=torch.float32, device=dev)
+    Yd = torch.zeros((nlg, P, w4.d), dtype=torch.float32, device=dev)
+    nact = torch.zeros((nlg, P), dtype=torch.int32, device=dev)
+    wsp, wsb = ws.data_ptr(), ws.numel()
+
+    def sparse_step(per, j, counts=False):
+        return [(lib.sparse_ffn_decode, (ctypes.byref(layers[l].c), X[per, l, j].data_ptr(), 1, t[l:l + 1].data_ptr(),
+                                         None, None, None, Ys[l, j].data_ptr(), None,
+                                         nact[l, j:j + 1].data_ptr() if counts else None, wsp, wsb))
+                for l in range(nlg)]
+
+    def verify(per):
+        return [(lib.ffn_dense_chunk, (ctypes.byref(layers[l].c), X[per, l].data_ptr(), P, Yd[l].data_ptr(), wsp, wsb))
+                for l in range(nlg)]
+
+    def dense_tokens(per):
+        return [(lib.ffn_dense_chunk, (ctypes.byref(layers[l].c), X[per, l, j].data_ptr(), 1, Ys[l, j].data_ptr(),
+                                       wsp, wsb)) for j in range(P) for l in range(nlg)]
+
+    def period(per, counts=False):
+        return [c for j in range(P) for c in sparse_step(per, j, counts)] + verify(per)
+    time_mixed(torch, [period(0)], mode)
+    per_ms = time_mixed(torch, [period(p) for p in range(1, n_per)], mode) / (n_per - 1)
+    sparse_ms = time_mixed(torch, [[c for j in range(P) for c in sparse_step(p, j)] for p in range(1, n_per)],
+                           mode) / (n_per - 1)
+    verify_ms = time_mixed(torch, [verify(p) for p in range(1, n_per)], mode) / (n_per - 1)
+    time_mixed(torch, [dense_tokens(0)], mode)
+    dense_ms = time_mixed(torch, [dense_tokens(p) for p in range(1, n_per)], mode) / (n_per - 1)
+    # outputs and active counts of the last period (untimed), then the statistics
+    for fn, a in period(n_per - 1, counts=True):
+        fn(*a, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    div = ((Ys - Yd).norm(dim=-1) / Yd.norm(dim=-1)).flatten().cpu().numpy()
+    dens = float(nact.float().mean().item()) / w4.f
+    rho = (1.0 + 2.0 * dens) / 3.0  # a CATS step's weight bytes over a dense token's
+    dense_tok_bytes = 6.0 * w4.f * w4.d * nlg
+    res = {"d": w4.d, "f": w4.f, "layers": nlg, "period": P, "sparsity": 0.5, "active_density": dens,
+           "period_ms": per_ms, "sparse_steps_ms": sparse_ms, "verify_ms": verify_ms,
+           "dense_decode_16_tokens_ms": dense_ms,
+           "divergence": {"mean": float(div.mean()), "p90": float(np.quantile(div, 0.9)), "max": float(div.max())}}
+    # accepted advance length: all 16, and 15.37 of 16 (the page's GSM8K figure)
+    for name, aal in (("aal16", 16.0), ("aal15.37", 15.37)):
+        res[name] = {"tokens_per_s": aal / (per_ms * 1e-3), "latency_vs_full": (per_ms / aal) / (dense_ms / P),
+                     "effective_density": (P * rho + 1.0) / aal,
+                     "effective_bytes_per_token": (P * rho + 1.0) * dense_tok_bytes / aal}
+    out["llama3_70b_sirius_period16"] = res
+    log(f"  extra sirius period: {per_ms:.3f} ms ({sparse_ms:.3f} sparse + {verify_ms:.3f} verify), dense 16 tokens "
+        f"{dense_ms:.3f} ms, latency vs full {res['aal16']['latency_vs_full']:.3f}, divergence mean "
+        f"{res['divergence']['mean']:.4f}")
+    del layers, ws, X, Ys, Yd
+    torch.cuda.empty_cache()
+
     # ReGLU layers with SVD predictors (factors and thresholds from the offline
     # preparation): the sequential pipeline with a rank-256 predictor (predict, then the
     # gate on the candidates and up/down where ReLU(gate) > 0) and the parallel pipeline

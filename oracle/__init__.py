@@ -15,7 +15,8 @@ Every function cites the passage of the source pages it follows:
   Table 4) -- rank-r SVD predictor of the gate, per-neuron thresholds, ReGLU
   sequential pipeline.
 * "SIRIUS: Contexual Sparisty with Correction for Efficient LLMs" (Approach, Key
-  results) -- the full model verifies a 16-token chunk with the shared weights.
+  results) -- the full model verifies a 16-token chunk with the shared weights; the
+  period's effective density and the sparse-to-full divergence of the layer outputs.
 
 Where the pages leave a step open the oracle takes the plainest reading; each reading is
 named in the docstring of the function that makes it.
@@ -52,3 +53,4 @@ from .svd import (  # noqa: F401
     calibrate_tau,
     reglu_sequential,
 )
+from .sirius import effective_density, sparse_dense_divergence, period_outputs  # noqa: F401

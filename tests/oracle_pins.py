@@ -366,4 +366,58 @@ def pin_tau_monotone():
         prev = dens
 
 
+def pin_effective_density():
+    """Hand-computed values of (period rho + rho_verify) / aal."""
+    ed = oracle.effective_density
+    assert ed(1.0, 16, 16) == 17.0 / 16.0  # a dense "sparse" step: the verification adds 1/16
+    assert abs(ed(2.0 / 3.0, 16, 16) - 35.0 / 48.0) <= 1e-15  # CATS at k 0.5 reads 2/3: (32/3 + 1)/16
+    assert ed(0.5, 16, 12) == 0.75  # (8 + 1) / 12
+    assert ed(0.5, 4, 4, rho_verify=0.0) == 0.5
+    for bad in ((0.5, 16, 17), (0.5, 16, 0.0), (0.5, 0, 1)):
+        try:
+            ed(*bad)
+        except ValueError:
+            continue
+        raise AssertionError(f"accepted {bad}")
+
+
+def pin_divergence():
+    """Hand-worked relative L2 distances, measured against the dense row."""
+    dv = oracle.sparse_dense_divergence
+    yd = np.array([[3.0, 4.0], [3.0, 4.0], [3.0, 4.0], [0.0, 0.0], [0.0, 0.0]])
+    ys = np.array([[3.0, 4.0], [4.5, 6.0], [3.0, 0.0], [0.0, 0.0], [1.0, 0.0]])
+    out = dv(ys, yd)
+    assert out[0] == 0.0 and out[1] == 0.5 and out[2] == 0.8 and out[3] == 0.0 and np.isinf(out[4])
+    assert dv(np.zeros((2, 3)), np.ones((2, 3))).tolist() == [1.0, 1.0]  # nothing active
+
+
+def pin_period_outputs():
+    """A period over two layers: with every neuron active (t = -1) the sparse steps equal
+    the verification exactly; with none active (t = inf) they are zero and the
+    divergence is 1; each layer's outputs depend on that layer only, and permuting the
+    chunk's tokens permutes its rows."""
+    g = np.random.default_rng(30)
+    d, f, P = 8, 20, 5
+    mk = lambda: tuple(g.standard_normal((f, d)) for _ in range(3))  # noqa: E731
+    layers = [mk(), mk()]
+    X = g.standard_normal((2, P, d))
+    ys, yd = oracle.period_outputs(layers, X, [-1.0, -1.0])
+    assert ys.shape == (2, P, d) and np.array_equal(ys, yd)
+    ys0, yd0 = oracle.period_outputs(layers, X, [np.inf, np.inf])
+    assert np.all(ys0 == 0.0) and np.array_equal(yd0, yd)
+    assert np.all(oracle.sparse_dense_divergence(ys0, yd0) == 1.0)
+    ys1, yd1 = oracle.period_outputs([layers[0], mk()], X, [0.05, 0.05])
+    ys2, yd2 = oracle.period_outputs(layers, X, [0.05, 0.05])
+    assert np.array_equal(ys1[0], ys2[0]) and np.array_equal(yd1[0], yd2[0])
+    perm = g.permutation(P)
+    ys3, yd3 = oracle.period_outputs(layers, X[:, perm], [0.05, 0.05])
+    assert np.array_equal(ys3, ys2[:, perm]) and np.array_equal(yd3, yd2[:, perm])
+    # one token by hand: the dense row is sum_i silu(g_i) u_i Dt[i]
+    Wg, Wu, Dt = layers[1]
+    x = X[1, 2]
+    gg, uu = Wg @ x, Wu @ x
+    h = gg / (1.0 + np.exp(-gg)) * uu
+    assert np.allclose(yd[1, 2], sum(h[i] * Dt[i] for i in range(f)), rtol=1e-13, atol=1e-13)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

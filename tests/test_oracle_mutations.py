@@ -12,6 +12,7 @@ import pytest
 import oracle
 import oracle.calibrate as ocal
 import oracle.ffn as offn
+import oracle.sirius as osir
 import oracle.svd as osvd
 from tests import oracle_pins
 
@@ -80,6 +81,21 @@ def _dense_ffn_transposed(Wg, Wu, Dt, x, act="silu", b=None):
     return (Dt @ h) if Dt.shape[1] == h.shape[0] else Dt.T @ h[::-1]
 
 
+def _eff_density_no_verify(rho_sparse, period, aal, rho_verify=1.0):
+    return float(rho_sparse) * int(period) / float(aal)
+
+
+def _eff_density_per_period(rho_sparse, period, aal, rho_verify=1.0):
+    return (int(period) * float(rho_sparse) + float(rho_verify)) / int(period)
+
+
+def _divergence_sparse_norm(y_sparse, y_dense):
+    ys, yd = np.asarray(y_sparse, float), np.asarray(y_dense, float)
+    den = np.sqrt(np.sum(ys ** 2, axis=-1))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.sqrt(np.sum((ys - yd) ** 2, axis=-1)) / den
+
+
 def _bf16_wrong_shift(bits):
     b = np.asarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
@@ -98,6 +114,12 @@ MUTATIONS = {
                              (oracle, "svd_factors_whitened", _whitened_no_back_map)],
     "whitened_transposed_root": [(osvd, "svd_factors_whitened", _whitened_transposed_root),
                                  (oracle, "svd_factors_whitened", _whitened_transposed_root)],
+    "eff_density_no_verify": [(osir, "effective_density", _eff_density_no_verify),
+                              (oracle, "effective_density", _eff_density_no_verify)],
+    "eff_density_per_period": [(osir, "effective_density", _eff_density_per_period),
+                               (oracle, "effective_density", _eff_density_per_period)],
+    "divergence_sparse_norm": [(osir, "sparse_dense_divergence", _divergence_sparse_norm),
+                               (oracle, "sparse_dense_divergence", _divergence_sparse_norm)],
     "down_transposed": [(offn, "dense_ffn", _dense_ffn_transposed), (oracle, "dense_ffn", _dense_ffn_transposed)],
     "bf16_decode_shift": [(offn, "bf16_to_f64", _bf16_wrong_shift), (oracle, "bf16_to_f64", _bf16_wrong_shift)],
 }
