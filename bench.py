@@ -74,6 +74,8 @@ def parse():
                     help="skip the other workloads (batch 4, SVD pipeline, 70B-shape decode and 16-token chunk)")
     ap.add_argument("--no-table4", action="store_true",
                     help="skip the fixed-sparsity protocol (random candidate subsets on every layer, three shapes)")
+    ap.add_argument("--no-quality", action="store_true",
+                    help="skip the predictor-quality diagnostics (ROC AUC and recall against rank and s)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before the stack, copy a MIB-MiB buffer three times (counter scaling)")
     ap.add_argument("--summarize-trace", metavar="DIR")
@@ -706,6 +708,11 @@ def main():
         log("fixed-sparsity protocol (predictor excluded)")
         t4 = table4(B, inputs, torch, args.mode)
 
+    quality = None
+    if not args.no_quality:
+        log("predictor quality (ROC AUC and recall against rank and s)")
+        quality = predictor_quality(B, inputs, torch)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -725,6 +732,7 @@ def main():
         "sweep": result_sweep,
         "extras": extra,
         "table4": t4,
+        "predictor_quality": quality,
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -787,6 +795,90 @@ def table4(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4,
     return {"protocol": "fixed sparsity on every layer and projection (gate included), uniformly drawn neuron "
                         "subsets per token and layer, predictor excluded; one-pass candidate path vs dense FFN call",
             "layers_timed": n_layers, "steps": n_steps, "rows": rows}
+
+
+def predictor_quality(B, inputs, torch, ranks=(16, 32, 64, 128, 256, 512, 1024), n_eval=256,
+                      svals=(0.1, 0.3, 0.5, 0.7, 0.9)):
+    """Predictor diagnostics on one ReGLU layer of the synthetic recipe ("SVD Contextual
+    Sparsity Predictors for Fast LLM Inference", Figures 2, 4, 5 and 7): ROC AUC of the
+    library's predictor outputs against the true activity (gate > 0, from the library's
+    own mask-only decode) at each rank, with plain and whitened factors; and recall,
+    false-negative rate and candidate density of the candidate sets at calibrated
+    thresholds for several s, and at the zero threshold. Two token distributions:
+    isotropic x ~ N(0, I) as everywhere else, and anisotropic x ~ N(0, R diag(e) R^T)
+    with eigenvalues e log-spaced over two decades, where whitening can matter."""
+    import numpy as np
+    from contextual_activation_sparsity_amd import diagnostics as dg
+    from contextual_activation_sparsity_amd import prepare
+    dev = "cuda"
+    w3 = inputs.workload(3)
+    d, f = w3.d, w3.f
+    gen = lambda sd: torch.Generator(device=dev).manual_seed(sd)  # noqa: E731
+    A = torch.randn((f, w3.rank), generator=gen(inputs.seed(3, 0, inputs.T_A)), device=dev) / np.sqrt(w3.rank)
+    Bm = torch.randn((w3.rank, d), generator=gen(inputs.seed(3, 0, inputs.T_B)), device=dev) * w3.w_std
+    noise = torch.randn((f, d), generator=gen(inputs.seed(3, 0, inputs.T_NOISE)), device=dev) * w3.w_std
+    wg = (A @ Bm + 0.1 * noise).to(torch.bfloat16)
+    del A, Bm, noise
+    bias = (-1.2815516 * wg.float().norm(dim=1)).contiguous()
+    wu = inputs.torch_gaussian_bf16((f, d), w3.w_std, inputs.seed(3, 0, inputs.T_UP), dev)
+    wd = inputs.torch_gaussian_bf16((f, d), w3.w_std, inputs.seed(3, 0, inputs.T_DOWN), dev)
+    layer = B.FFNLayer(wg, wu, wd, b_gate=bias, act=B.SFN_ACT_RELU)
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, 1))
+    zero = torch.zeros(1, dtype=torch.float32, device=dev)
+    n_cal = 2 * d
+    z = torch.randn((n_cal + n_eval, d), generator=gen(1_000_000 * 3 + inputs.STREAM_TAU), device=dev)
+    Rm, _ = torch.linalg.qr(torch.randn((d, d), generator=gen(1_000_000 * 3 + 999_005), device=dev))
+    e = torch.logspace(-1.0, 1.0, d, device=dev)
+    e = e * (d / e.sum())  # mean eigenvalue 1, so the gate scale is unchanged on average
+    out = {"layer": "reglu d 4096 f 11008, gate rank 256 + noise", "eval_tokens": n_eval,
+           "calibration_tokens": n_cal, "ranks": list(ranks), "tokens": {}}
+    for tname, X in (("isotropic", z), ("anisotropic", (z * e.sqrt()) @ Rm.T)):
+        X = X.to(torch.bfloat16)
+        xc, xe = X[:n_cal], X[n_cal:]
+        # true activity of the evaluation tokens from the library: ReLU(g) > 0
+        idx = torch.zeros((n_eval, f), dtype=torch.int32, device=dev)
+        cnt = torch.zeros(n_eval, dtype=torch.int32, device=dev)
+        for j in range(n_eval):
+            B.sparse_ffn_decode(layer, xe[j:j + 1], zero, ws, y=None, active_idx=idx[j:j + 1], n_active=cnt[j:j + 1])
+        act = dg.masks_from_lists(idx, cnt, f)
+        gcal = xc.float() @ wg.float().t() + bias
+        res = {"active_density": float(act.float().mean().item()), "auc": {}, "thresholds": []}
+        for whiten in (False, True):
+            facs = prepare.svd_factors_ranks(wg, ranks, x_cal=xc if whiten else None)
+            aucs = {}
+            for r, (q, lf) in facs.items():
+                pred = B.SVDPredictor(q, lf, torch.zeros(f, dtype=torch.float32, device=dev), b=bias)
+                wsp = B.workspace(B.svd_predict_workspace_size(pred))
+                P = torch.zeros((n_eval, f), dtype=torch.float32, device=dev)
+                cand = torch.zeros(f, dtype=torch.int32, device=dev)
+                nc = torch.zeros(1, dtype=torch.int32, device=dev)
+                for j in range(n_eval):
+                    B.svd_predict(pred, xe[j:j + 1], cand, nc, wsp, p_out=P[j])
+                aucs[r] = dg.roc_auc(P, act)
+                if r in (256, 1024):
+                    pcal = prepare.predictions(q, lf, xc.float(), bias)
+                    for sv in (None,) + tuple(svals):
+                        tau = (torch.zeros(f, dtype=torch.float32, device=dev) if sv is None
+                               else prepare.calibrate_tau(pcal, gcal, sv))
+                        pr = B.SVDPredictor(q, lf, tau, b=bias)
+                        ci = torch.zeros((n_eval, f), dtype=torch.int32, device=dev)
+                        cc = torch.zeros(n_eval, dtype=torch.int32, device=dev)
+                        for j in range(n_eval):
+                            B.svd_predict(pr, xe[j:j + 1], ci[j], cc[j:j + 1], wsp)
+                        cm = dg.masks_from_lists(ci, cc, f)
+                        rc = dg.recall(cm, act)
+                        res["thresholds"].append({"r": r, "whitened": whiten, "s": sv if sv is not None else "zero",
+                                                  "recall": rc, "false_negative_rate": 1.0 - rc,
+                                                  "candidate_density": float(cm.float().mean().item())})
+                    del pcal
+            res["auc"]["whitened" if whiten else "plain"] = aucs
+            log(f"  {tname} tokens, {'whitened' if whiten else 'plain'} factors: AUC "
+                + " ".join(f"r{r} {a:.4f}" for r, a in aucs.items()))
+        for t in res["thresholds"]:
+            log(f"    r {t['r']} {'whitened' if t['whitened'] else 'plain'} s {t['s']}: recall {t['recall']:.4f}, "
+                f"candidates {t['candidate_density']:.3f}")
+        out["tokens"][tname] = res
+    return out
 
 
 def write_traffic(dirs, probe, command):

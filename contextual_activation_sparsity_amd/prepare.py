@@ -7,13 +7,45 @@ Figure 1): a low-rank SVD predictor with calibrated per-neuron thresholds, built
 offline; Table 3 adds data whitening.
 """
 
-from typing import Optional, Tuple
+from typing import Dict, Optional, Tuple
 
 import torch
 
 
 def _work_dtype(t: torch.Tensor) -> torch.dtype:
     return torch.float64 if t.device.type == "cpu" else torch.float32
+
+
+def _decompose(w_gate: torch.Tensor, x_cal: Optional[torch.Tensor], ridge: float):
+    """(U, s, Vh, S): the SVD of w_gate, or of w_gate S with S the Cholesky factor of the
+    calibration tokens' second moment (S None without whitening)."""
+    wd = _work_dtype(w_gate)
+    W = w_gate.to(wd)
+    if x_cal is None:
+        U, s, Vh = torch.linalg.svd(W, full_matrices=False)
+        return U, s, Vh, None
+    X = x_cal.to(device=W.device, dtype=wd)
+    if X.ndim != 2 or X.shape[1] != W.shape[1] or X.shape[0] < X.shape[1]:
+        # with fewer tokens than d the second moment is singular: the ridge alone then
+        # decides the factors, and in fp32 the Cholesky factorization can fail
+        raise ValueError("whitening needs calibration tokens x_cal [n, d] with n >= d")
+    C = X.T @ X / X.shape[0]
+    C = C + ridge * torch.trace(C) / C.shape[0] * torch.eye(C.shape[0], dtype=wd, device=W.device)
+    S = torch.linalg.cholesky(C)
+    U, s, Vh = torch.linalg.svd(W @ S, full_matrices=False)
+    return U, s, Vh, S
+
+
+def _truncate(U, s, Vh, S, r: int, dtype: torch.dtype) -> Tuple[torch.Tensor, torch.Tensor]:
+    if not (1 <= r <= s.numel()):
+        raise ValueError("rank r must lie in [1, min(f, d)]")
+    if S is None:
+        q = Vh[:r]
+    else:
+        # q = V_r^T S^{-1}, i.e. S^T q^T = V_r
+        q = torch.linalg.solve_triangular(S.T, Vh[:r].T, upper=True).T
+    lf = U[:, :r] * s[:r]
+    return q.to(dtype).contiguous(), lf.to(dtype).contiguous()
 
 
 def svd_factors(w_gate: torch.Tensor, r: int, x_cal: Optional[torch.Tensor] = None, ridge: float = 1e-6,
@@ -27,27 +59,19 @@ def svd_factors(w_gate: torch.Tensor, r: int, x_cal: Optional[torch.Tensor] = No
     ridge), take the truncated SVD of w_gate S and map it back: q = V_r^T S^{-1}.
     Whitening needs at least d calibration tokens.
     """
-    wd = _work_dtype(w_gate)
-    W = w_gate.to(wd)
-    if not (1 <= r <= min(W.shape)):
+    if not (1 <= r <= min(w_gate.shape)):
         raise ValueError("rank r must lie in [1, min(f, d)]")
-    if x_cal is None:
-        U, s, Vh = torch.linalg.svd(W, full_matrices=False)
-        q = Vh[:r]
-    else:
-        X = x_cal.to(device=W.device, dtype=wd)
-        if X.ndim != 2 or X.shape[1] != W.shape[1] or X.shape[0] < X.shape[1]:
-            # with fewer tokens than d the second moment is singular: the ridge alone then
-            # decides the factors, and in fp32 the Cholesky factorization can fail
-            raise ValueError("whitening needs calibration tokens x_cal [n, d] with n >= d")
-        C = X.T @ X / X.shape[0]
-        C = C + ridge * torch.trace(C) / C.shape[0] * torch.eye(C.shape[0], dtype=wd, device=W.device)
-        S = torch.linalg.cholesky(C)
-        U, s, Vh = torch.linalg.svd(W @ S, full_matrices=False)
-        # q = V_r^T S^{-1}, i.e. S^T q^T = V_r
-        q = torch.linalg.solve_triangular(S.T, Vh[:r].T, upper=True).T
-    lf = U[:, :r] * s[:r]
-    return q.to(dtype).contiguous(), lf.to(dtype).contiguous()
+    return _truncate(*_decompose(w_gate, x_cal, ridge), r, dtype)
+
+
+def svd_factors_ranks(w_gate: torch.Tensor, ranks, x_cal: Optional[torch.Tensor] = None, ridge: float = 1e-6,
+                      dtype: torch.dtype = torch.bfloat16) -> Dict[int, Tuple[torch.Tensor, torch.Tensor]]:
+    """svd_factors at several ranks from one decomposition: {r: (q, l)}."""
+    ranks = [int(r) for r in ranks]
+    if any(not (1 <= r <= min(w_gate.shape)) for r in ranks):
+        raise ValueError("rank r must lie in [1, min(f, d)]")
+    dec = _decompose(w_gate, x_cal, ridge)
+    return {r: _truncate(*dec, r, dtype) for r in ranks}
 
 
 def predictions(q: torch.Tensor, lf: torch.Tensor, x: torch.Tensor, b: Optional[torch.Tensor] = None) -> torch.Tensor:

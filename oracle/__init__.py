@@ -13,7 +13,8 @@ Every function cites the passage of the source pages it follows:
   (abstract) -- thresholded SiLU activation, calibrated threshold.
 * "SVD Contextual Sparsity Predictors for Fast LLM Inference" (abstract, Figures 1-3,
   Table 4) -- rank-r SVD predictor of the gate, per-neuron thresholds, ReGLU
-  sequential pipeline.
+  sequential pipeline, whitened factors; predictor quality (ROC AUC, recall;
+  Figures 2, 4, 5 and 7).
 * "SIRIUS: Contexual Sparisty with Correction for Efficient LLMs" (Approach, Key
   results) -- the full model verifies a 16-token chunk with the shared weights; the
   period's effective density and the sparse-to-full divergence of the layer outputs.
@@ -54,3 +55,4 @@ from .svd import (  # noqa: F401
     reglu_sequential,
 )
 from .sirius import effective_density, sparse_dense_divergence, period_outputs  # noqa: F401
+from .diagnostics import roc_auc, recall, false_negative_rate  # noqa: F401

@@ -420,4 +420,43 @@ def pin_period_outputs():
     assert np.allclose(yd[1, 2], sum(h[i] * Dt[i] for i in range(f)), rtol=1e-13, atol=1e-13)
 
 
+def pin_roc_auc_brute_force():
+    """Against the definition counted pair by pair (ties one half) on small integer
+    scores with many ties."""
+    g = np.random.default_rng(31)
+    for n in (7, 20, 41):
+        sc = g.integers(0, 5, size=n).astype(float)
+        lab = g.random(n) < 0.4
+        lab[0], lab[1] = True, False
+        pos, neg = sc[lab], sc[~lab]
+        wins = 0.0
+        for a in pos:
+            for b in neg:
+                wins += 1.0 if a > b else (0.5 if a == b else 0.0)
+        assert abs(oracle.roc_auc(sc, lab) - wins / (len(pos) * len(neg))) <= 1e-12
+
+
+def pin_roc_auc_closed_forms():
+    """Separated classes give 1, reversed 0, all tied 1/2; for positives N(mu, 1) against
+    negatives N(0, 1) the AUC is Phi(mu / sqrt 2)."""
+    lab = np.array([False, False, True, True, True])
+    assert oracle.roc_auc([0.1, 0.2, 0.3, 0.4, 0.5], lab) == 1.0
+    assert oracle.roc_auc([0.5, 0.4, 0.3, 0.2, 0.1], lab) == 0.0
+    assert oracle.roc_auc(np.zeros(5), lab) == 0.5
+    g = np.random.default_rng(32)
+    for mu in (0.0, 0.5, 1.5):
+        neg, pos = g.standard_normal(20000), g.standard_normal(20000) + mu
+        auc = oracle.roc_auc(np.concatenate([neg, pos]), np.r_[np.zeros(20000, bool), np.ones(20000, bool)])
+        assert abs(auc - stats.norm.cdf(mu / math.sqrt(2.0))) <= 0.01, (mu, auc)
+
+
+def pin_recall():
+    """Hand-worked pooled recall over two tokens."""
+    act = np.array([[1, 1, 0, 0, 1], [0, 1, 1, 0, 0]], bool)
+    cand = np.array([[1, 0, 1, 0, 1], [0, 1, 0, 1, 0]], bool)
+    assert oracle.recall(cand, act) == 3.0 / 5.0
+    assert abs(oracle.false_negative_rate(cand, act) - 0.4) <= 1e-15
+    assert oracle.recall(np.ones_like(act), act) == 1.0
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

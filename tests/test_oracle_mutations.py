@@ -11,6 +11,7 @@ import pytest
 
 import oracle
 import oracle.calibrate as ocal
+import oracle.diagnostics as odia
 import oracle.ffn as offn
 import oracle.sirius as osir
 import oracle.svd as osvd
@@ -96,6 +97,25 @@ def _divergence_sparse_norm(y_sparse, y_dense):
         return np.sqrt(np.sum((ys - yd) ** 2, axis=-1)) / den
 
 
+def _auc_ties_win(scores, labels):
+    from scipy import stats
+    s, y = np.asarray(scores, float).ravel(), np.asarray(labels, bool).ravel()
+    n1, n0 = int(y.sum()), int((~y).sum())
+    return float((stats.rankdata(s, method="max")[y].sum() - n1 * (n1 + 1) / 2.0) / (n1 * n0))
+
+
+def _auc_reference_swapped(scores, labels):
+    from scipy import stats
+    s, y = np.asarray(scores, float).ravel(), ~np.asarray(labels, bool).ravel()
+    n1, n0 = int(y.sum()), int((~y).sum())
+    return float((stats.rankdata(s)[y].sum() - n1 * (n1 + 1) / 2.0) / (n1 * n0))
+
+
+def _recall_as_precision(candidates, active):
+    c, a = np.asarray(candidates, bool), np.asarray(active, bool)
+    return float(np.logical_and(c, a).sum() / c.sum())
+
+
 def _bf16_wrong_shift(bits):
     b = np.asarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
@@ -120,6 +140,9 @@ MUTATIONS = {
                                (oracle, "effective_density", _eff_density_per_period)],
     "divergence_sparse_norm": [(osir, "sparse_dense_divergence", _divergence_sparse_norm),
                                (oracle, "sparse_dense_divergence", _divergence_sparse_norm)],
+    "auc_ties_count_as_wins": [(odia, "roc_auc", _auc_ties_win), (oracle, "roc_auc", _auc_ties_win)],
+    "auc_classes_swapped": [(odia, "roc_auc", _auc_reference_swapped), (oracle, "roc_auc", _auc_reference_swapped)],
+    "recall_as_precision": [(odia, "recall", _recall_as_precision), (oracle, "recall", _recall_as_precision)],
     "down_transposed": [(offn, "dense_ffn", _dense_ffn_transposed), (oracle, "dense_ffn", _dense_ffn_transposed)],
     "bf16_decode_shift": [(offn, "bf16_to_f64", _bf16_wrong_shift), (oracle, "bf16_to_f64", _bf16_wrong_shift)],
 }

@@ -65,3 +65,12 @@ def test_whitening_rejects_too_few_tokens():
             prepare.svd_factors(torch.from_numpy(Wg), 4, x_cal=torch.from_numpy(bad))
     with pytest.raises(ValueError):
         prepare.svd_factors(torch.from_numpy(Wg), Wg.shape[1] + 1)
+
+
+def test_factors_at_several_ranks_match_single_rank():
+    Wg, X = _case(6)
+    for xc in (None, torch.from_numpy(X)):
+        multi = prepare.svd_factors_ranks(torch.from_numpy(Wg), (2, 9, 32), x_cal=xc, dtype=torch.float64)
+        for r, (q, lf) in multi.items():
+            q1, l1 = prepare.svd_factors(torch.from_numpy(Wg), r, x_cal=xc, dtype=torch.float64)
+            assert np.allclose(lf.numpy() @ q.numpy(), l1.numpy() @ q1.numpy(), atol=1e-12)
