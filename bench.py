@@ -542,6 +542,26 @@ def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4):
         if r == 256:
             out[name]["active_density"] = na / f
         log(f"  extra {name}: {us:.2f} us/layer (predictor {pred_us:.2f}), cand {out[name]['candidate_density']:.3f}")
+
+    # the same two pipelines through the fused call: each tile predicts its own rows and
+    # processes its candidates, no candidate list in between (same bytes)
+    wsf = B.workspace(max(B.sparse_ffn_svd_workspace_size(layers[0], pred_seq[0]),
+                          B.sparse_ffn_svd_workspace_size(layers[0], pred_par[0])))
+
+    def fused(preds, pipe):
+        return lambda tok, l: [(lib.sparse_ffn_decode_svd, (ctypes.byref(layers[l].c), ctypes.byref(preds[l].c),
+                                                            X[tok, l].data_ptr(), pipe, y[l].data_ptr(), None, None,
+                                                            wsf.data_ptr(), wsf.numel()))]
+    for name, base, calls in (("reglu_svd_r256_s50_fused", "reglu_svd_r256_s50", fused(pred_seq, B.SFN_PIPE_SEQUENTIAL)),
+                              ("reglu_svd_r1024_whitened_parallel_fused", "reglu_svd_r1024_whitened_parallel",
+                               fused(pred_par, B.SFN_PIPE_PARALLEL))):
+        us = leg(calls)
+        byts = out[base]["algorithmic_bytes_per_layer"]
+        out[name] = {"d": d, "f": f, "r": out[base]["r"], "s": w3.s, "layers_timed": n_layers, "us_per_layer": us,
+                     "algorithmic_bytes_per_layer": byts, "gbs": byts / (us * 1e-6) / 1e9,
+                     "tokens_per_s_32_layers": 1.0 / (32 * us * 1e-6), "speedup_over_unfused": out[base]["us_per_layer"] / us}
+        log(f"  extra {name}: {us:.2f} us/layer ({out[name]['gbs']:.0f} GB/s), "
+            f"{out[name]['speedup_over_unfused']:.2f}x the unfused calls")
     return out
 
 

@@ -30,6 +30,7 @@ SFN_EWORKSPACE, SFN_EALIGN, SFN_EUNSUPPORTED, SFN_EHIP = -4, -5, -6, -7
 SFN_F32, SFN_BF16 = 0, 1
 SFN_ACT_SILU, SFN_ACT_RELU = 0, 1
 SFN_MAX_BATCH, SFN_MAX_CHUNK = 4, 16
+SFN_PIPE_SEQUENTIAL, SFN_PIPE_PARALLEL = 0, 1
 
 EXPORTED = (
     "sparse_ffn_workspace_size",
@@ -38,6 +39,8 @@ EXPORTED = (
     "sparse_ffn_calibrate",
     "sparse_ffn_decode",
     "sparse_ffn_decode_parallel",
+    "sparse_ffn_svd_workspace_size",
+    "sparse_ffn_decode_svd",
     "svd_predict",
     "ffn_dense_chunk",
 )
@@ -71,6 +74,11 @@ _lib.sparse_ffn_decode.argtypes = [ctypes.POINTER(sfn_ffn), _vp, _i32, _vp, _vp,
 _lib.sparse_ffn_decode.restype = ctypes.c_int
 _lib.sparse_ffn_decode_parallel.argtypes = [ctypes.POINTER(sfn_ffn), _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.sparse_ffn_decode_parallel.restype = ctypes.c_int
+_lib.sparse_ffn_svd_workspace_size.argtypes = [ctypes.POINTER(sfn_ffn), ctypes.POINTER(sfn_svd)]
+_lib.sparse_ffn_svd_workspace_size.restype = _sz
+_lib.sparse_ffn_decode_svd.argtypes = [ctypes.POINTER(sfn_ffn), ctypes.POINTER(sfn_svd), _vp, _i32, _vp, _vp, _vp, _vp,
+                                       _sz, _vp]
+_lib.sparse_ffn_decode_svd.restype = ctypes.c_int
 _lib.svd_predict.argtypes = [ctypes.POINTER(sfn_svd), _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.svd_predict.restype = ctypes.c_int
 _lib.ffn_dense_chunk.argtypes = [ctypes.POINTER(sfn_ffn), _vp, _i32, _vp, _vp, _sz, _vp]
@@ -213,6 +221,20 @@ def sparse_ffn_decode_parallel(layer: FFNLayer, x: torch.Tensor, cand: torch.Ten
         _ptr(n_cand, "n_cand", torch.int32, 1), _ptr(y, "y", torch.float32, layer.d), _ptr(ws, "ws"),
         ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "sparse_ffn_decode_parallel")
+
+
+def sparse_ffn_svd_workspace_size(layer: FFNLayer, pred: SVDPredictor) -> int:
+    return int(_lib.sparse_ffn_svd_workspace_size(ctypes.byref(layer.c), ctypes.byref(pred.c)))
+
+
+def sparse_ffn_decode_svd(layer: FFNLayer, pred: SVDPredictor, x: torch.Tensor, ws: torch.Tensor,
+                          y: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                          n_idx: Optional[torch.Tensor] = None, pipeline: int = SFN_PIPE_SEQUENTIAL, stream=None):
+    st = _lib.sparse_ffn_decode_svd(
+        ctypes.byref(layer.c), ctypes.byref(pred.c), _ptr(x, "x", torch.bfloat16, layer.d), int(pipeline),
+        _ptr(y, "y", torch.float32, layer.d), _ptr(idx, "idx", torch.int32, layer.f),
+        _ptr(n_idx, "n_idx", torch.int32, 1), _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "sparse_ffn_decode_svd")
 
 
 def svd_predict(pred: SVDPredictor, x: torch.Tensor, cand_idx: torch.Tensor, n_cand: torch.Tensor,

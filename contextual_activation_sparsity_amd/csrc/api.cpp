@@ -215,6 +215,87 @@ int svd_predict(const sfn_svd* svd, const void* x, int32_t* cand_idx, int32_t* n
   }
 }
 
+namespace {
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Fused SVD pipeline workspace: the decode scratch for one token, then z [r] fp32.
+size_t svd_pipeline_z_offset(const sfn_ffn* ffn) { return round256(sfn::decode_workspace_bytes(ffn->d, ffn->f, 2, 1)); }
+size_t svd_pipeline_bytes(const sfn_ffn* ffn, const sfn_svd* svd) {
+  return svd_pipeline_z_offset(ffn) + round256((size_t)svd->r * sizeof(float));
+}
+
+int check_svd_pipeline(const sfn_ffn* ffn, const sfn_svd* svd) {
+  int st = check_ffn(ffn, true);
+  if (st != SFN_OK) return st;
+  st = check_svd(svd);
+  if (st != SFN_OK) return st;
+  if (ffn->wdtype != SFN_BF16) return SFN_EDTYPE;  // the predictor takes the bf16 token
+  if (svd->d != ffn->d || svd->f != ffn->f) return SFN_ESHAPE;
+  return SFN_OK;
+}
+
+}  // namespace
+
+size_t sparse_ffn_svd_workspace_size(const sfn_ffn* ffn, const sfn_svd* svd) {
+  try {
+    if (check_svd_pipeline(ffn, svd) != SFN_OK) return 0;
+    return svd_pipeline_bytes(ffn, svd);
+  } catch (...) {
+    return 0;
+  }
+}
+
+int sparse_ffn_decode_svd(const sfn_ffn* ffn, const sfn_svd* svd, const void* x, int32_t pipeline, float* y,
+                          int32_t* idx, int32_t* n_idx, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    int st = check_svd_pipeline(ffn, svd);
+    if (st != SFN_OK) return st;
+    if (!x) return SFN_EINVAL;
+    if (pipeline != SFN_PIPE_SEQUENTIAL && pipeline != SFN_PIPE_PARALLEL) return SFN_EINVAL;
+    if (pipeline == SFN_PIPE_PARALLEL && !y) return SFN_EINVAL;
+    if (!y && !idx && !n_idx) return SFN_EINVAL;  // nothing to compute
+    if (!aligned16(x)) return SFN_EALIGN;
+    if (y && !aligned16(y)) return SFN_EALIGN;
+    if ((idx && (reinterpret_cast<uintptr_t>(idx) & 3u)) || (n_idx && (reinterpret_cast<uintptr_t>(n_idx) & 3u)))
+      return SFN_EALIGN;
+    st = check_ws(ws, ws_bytes, svd_pipeline_bytes(ffn, svd));
+    if (st != SFN_OK) return st;
+
+    float* z = reinterpret_cast<float*>(static_cast<char*>(ws) + svd_pipeline_z_offset(ffn));
+    sfn::DecodeArgs a{};
+    a.wg = static_cast<const char*>(ffn->w_gate);
+    a.wu = static_cast<const char*>(ffn->w_up);
+    a.wd = static_cast<const char*>(ffn->w_down_t);
+    a.bias = ffn->b_gate;
+    a.x = static_cast<const char*>(x);
+    a.y = y;
+    a.active_idx = idx;
+    a.n_active = n_idx;
+    a.pl = static_cast<const char*>(svd->l);
+    a.pz = z;
+    a.ptau = svd->tau;
+    a.pb = svd->b;
+    a.pr = svd->r;
+    a.d = ffn->d;
+    a.f = ffn->f;
+    a.nch = ffn->d * 2 / 16;
+    a.row_bytes = ffn->d * 2;
+    a.nb = 1;
+    a.act = ffn->act;
+    a.G = sfn::decode_grid(ffn->f);
+    a.n_red = sfn::decode_reducers(a.G, 1, ffn->d);
+    sfn::decode_carve(a, ws, 2);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = sfn::launch_svd_z(*svd, x, z, s);
+    if (e != hipSuccess) return SFN_EHIP;
+    e = pipeline == SFN_PIPE_PARALLEL ? sfn::launch_decode_parallel(a, SFN_BF16, s) : sfn::launch_decode(a, SFN_BF16, s);
+    return hip_status(e);
+  } catch (...) {
+    return SFN_EHIP;
+  }
+}
+
 int ffn_dense_chunk(const sfn_ffn* ffn, const void* x, int32_t n, float* y, void* ws, size_t ws_bytes,
                     void* stream) {
   try {

@@ -77,6 +77,11 @@ struct DevArgs {
   SFN_GLOBAL float* sel_a;
   SFN_GLOBAL uint8_t* sel_bits;
   SFN_GLOBAL float* part;
+  const SFN_GLOBAL char* pl;
+  const SFN_GLOBAL float* pz;
+  const SFN_GLOBAL float* ptau;
+  const SFN_GLOBAL float* pb;
+  int pr;
   int d, f, nch, row_bytes, nb, act, G, n_red;
 };
 
@@ -87,6 +92,7 @@ __device__ __forceinline__ DevArgs dev_args(const DecodeArgs& h) {
   a.active_idx = gp(h.active_idx); a.n_active = gp(h.n_active);
   a.tile_cnt = gp(h.tile_cnt); a.tile_idx = gp(h.tile_idx); a.sel_idx = gp(h.sel_idx); a.sel_a = gp(h.sel_a);
   a.sel_bits = gp(h.sel_bits); a.part = gp(h.part);
+  a.pl = gp(h.pl); a.pz = gp(h.pz); a.ptau = gp(h.ptau); a.pb = gp(h.pb); a.pr = h.pr;
   a.d = h.d; a.f = h.f; a.nch = h.nch; a.row_bytes = h.row_bytes; a.nb = h.nb; a.act = h.act; a.G = h.G;
   a.n_red = h.n_red;
   return a;
@@ -159,6 +165,97 @@ struct Shape {
   }
 };
 
+// ------------------------------------------------------------------ predictor phase
+// Predict mode: the SVD predictor on one tile's own rows ("SVD Contextual Sparsity
+// Predictors for Fast LLM Inference", Figures 1 and 3): p_i = L_i z + b_i for rows
+// [r0, r0 + nt) (z = Q x, computed by the launch before), candidates {i : p_i > tau_i},
+// compacted in ascending order into rowid[0, n). The tile then processes its own
+// candidates, so no candidate list crosses workgroups and no scan over tiles is needed.
+// Each row of L (r bf16 = r/8 chunks) is read by 2^lt lanes of one wave, at most two
+// chunks each (r <= 1024); 8 passes of rows are in flight per lane.
+struct PredSmem {
+  float p[kTMax];
+  int wcnt[kNW];
+  int n;
+};
+
+__device__ __forceinline__ float dot_l_z(const uint4& w, const float (&z)[8], float acc) {
+  const uint32_t p4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    acc = fmaf(__uint_as_float(p4[j] << 16), z[2 * j], acc);
+    acc = fmaf(__uint_as_float(p4[j] & 0xffff0000u), z[2 * j + 1], acc);
+  }
+  return acc;
+}
+
+__device__ void predict_tile(const DevArgs& a, PredSmem& ps, int r0, int nt, int* rowid) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // bias and threshold of row tid, read first (the compare below runs on thread tid)
+  float pb = 0.f, pt = 0.f;
+  if (tid < nt) {
+    pb = a.pb ? a.pb[r0 + tid] : 0.f;
+    pt = a.ptau[r0 + tid];
+  }
+  const int nchr = a.pr >> 3;
+  const int lt = nchr <= 8 ? 3 : nchr <= 16 ? 4 : nchr <= 32 ? 5 : 6;  // log2 lanes per row
+  const int tpr = 1 << lt;
+  const int rp = kNT >> lt;  // rows per pass
+  const int rl = tid >> lt, cl = tid & (tpr - 1);
+  float zc[2][8];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch = cl + tpr * c;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) zc[c][j] = ch < nchr ? a.pz[ch * 8 + j] : 0.f;
+  }
+  const size_t rb = (size_t)a.pr * 2;
+  const int npass = (nt + rp - 1) / rp;
+  for (int p0 = 0; p0 < npass; p0 += 8) {
+    uint4 wv[8][2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = (p0 + u) * rp + rl;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int ch = cl + tpr * c;
+        wv[u][c] = (row < nt && ch < nchr) ? ldg16(a.pl + (size_t)(r0 + row) * rb + (size_t)ch * 16)
+                                           : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float acc = dot_l_z(wv[u][1], zc[1], dot_l_z(wv[u][0], zc[0], 0.f));
+      for (int m = 1; m < tpr; m <<= 1) acc += __shfl_xor(acc, m, 64);
+      const int row = (p0 + u) * rp + rl;
+      if (cl == 0 && row < nt) ps.p[row] = acc;
+    }
+  }
+  __syncthreads();
+  // compare and compact, one wave per 64 rows (nt <= kTMax = 4 waves)
+  const int nw = (nt + 63) >> 6;
+  bool on = false;
+  unsigned long long bal = 0ull;
+  if (wave < nw) {
+    on = tid < nt && ps.p[tid] + pb > pt;
+    bal = __ballot(on);
+    if (lane == 0) ps.wcnt[wave] = (int)__popcll(bal);
+  }
+  __syncthreads();
+  if (on) {
+    int base = 0;
+    for (int w2 = 0; w2 < wave; ++w2) base += ps.wcnt[w2];
+    rowid[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0))] =
+        r0 + tid;
+  }
+  if (tid == 0) {
+    int n = 0;
+    for (int w2 = 0; w2 < nw; ++w2) n += ps.wcnt[w2];
+    ps.n = n;
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------------------------ gate kernel
 template <int WT, int BMAX, int CPT, int TPR, int R>
 struct GateKernel {
@@ -167,10 +264,11 @@ struct GateKernel {
   static constexpr int RPG = S::RPG, RG = S::RG, RS = S::RS, VG = S::VG;
 
   struct Smem {
-    int rowid[kTMax];  // candidate mode: global row of each local row
+    int rowid[kTMax];  // candidate and predict modes: global row of each local row
     float wpart[kNW][VG];
     int qlen;
     int cnt[BMAX];
+    PredSmem ps;
   };
 
   // Loads of one gate step: w0 = rows [base, base+RG), w1 = rows [base+RG, base+RS) of Wg,
@@ -216,12 +314,19 @@ struct GateKernel {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rl = tid / TPR, cl = tid % TPR;
     const int w = blockIdx.x;
-    const bool cand_mode = a.cand != nullptr;
+    const bool pred_mode = a.pl != nullptr;
+    const bool cand_mode = a.cand != nullptr || pred_mode;
     const bool want_idx = a.active_idx != nullptr || a.n_active != nullptr;
     const int nb = a.nb;
 
     int r0, nrows;
-    if (cand_mode) {
+    if (pred_mode) {
+      // the tile's own rows; its candidates become the local rows (the slices of the
+      // lists stay at the tile's first row)
+      r0 = share_begin(w, a.f, a.G);
+      predict_tile(a, sm.ps, r0, share_begin(w + 1, a.f, a.G) - r0, sm.rowid);
+      nrows = sm.ps.n;
+    } else if (cand_mode) {
       const int n = min(max(*a.n_cand, 0), a.f);  // a count beyond f cannot be a valid list
       r0 = share_begin(w, n, a.G);
       nrows = share_begin(w + 1, n, a.G) - r0;
@@ -554,6 +659,7 @@ struct ParKernel {
     float qb[kTMax];
     float wpart[kNW][V2];
     float h[64];
+    PredSmem ps;
   };
 
   // Loads of one step: Wg, Wu and Dt rows of share entries [base, base + n), or (step
@@ -588,13 +694,28 @@ struct ParKernel {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rl = tid / TPR, cl = tid % TPR;
     const int w = blockIdx.x;
-    const int n = min(max(*a.n_cand, 0), a.f);  // a count beyond f cannot be a valid list
-    const int s0 = share_begin(w, n, a.G);
-    const int nq = share_begin(w + 1, n, a.G) - s0;
-    for (int j = tid; j < nq; j += kNT) {
-      const int row = min(max(a.cand[s0 + j], 0), a.f - 1);  // in bounds
-      sm.qrow[j] = row;
-      sm.qb[j] = a.bias ? a.bias[row] : 0.f;
+    int nq;
+    if (a.pl) {
+      // predict mode: the candidates among the tile's own rows, also written to the
+      // tile's slice of the index lists (for the reduce kernel to assemble)
+      const int r0 = share_begin(w, a.f, a.G);
+      predict_tile(a, sm.ps, r0, share_begin(w + 1, a.f, a.G) - r0, sm.qrow);
+      nq = sm.ps.n;
+      for (int j = tid; j < nq; j += kNT) {
+        const int row = sm.qrow[j];
+        sm.qb[j] = a.bias ? a.bias[row] : 0.f;
+        a.tile_idx[r0 + j] = row;
+      }
+      if (tid < kCnt) a.tile_cnt[w * kCnt + tid] = tid < 2 ? nq : 0;
+    } else {
+      const int n = min(max(*a.n_cand, 0), a.f);  // a count beyond f cannot be a valid list
+      const int s0 = share_begin(w, n, a.G);
+      nq = share_begin(w + 1, n, a.G) - s0;
+      for (int j = tid; j < nq; j += kNT) {
+        const int row = min(max(a.cand[s0 + j], 0), a.f - 1);  // in bounds
+        sm.qrow[j] = row;
+        sm.qb[j] = a.bias ? a.bias[row] : 0.f;
+      }
     }
     float acc[CPT][KV];
 #pragma unroll

@@ -36,6 +36,14 @@ struct DecodeArgs {
   float* sel_a;       // [4, f]: their activations
   uint8_t* sel_bits;  // [f]: their per-token mask bits
   float* part;        // [G * rows side by side, nb, d]
+  // Predict mode (pl non-null; one token): each tile's candidates are {i : L_i z + pb_i >
+  // ptau_i} over its own rows instead of a share of a candidate list; z = Q x from the
+  // predictor's first launch, r = rank.
+  const char* pl;     // [f, r] bf16
+  const float* pz;    // [r]
+  const float* ptau;  // [f]
+  const float* pb;    // [f] or null
+  int pr;
   int d, f, nch, row_bytes, nb, act, G, n_red;
 };
 
@@ -61,6 +69,8 @@ hipError_t launch_calibrate(const sfn_ffn& ffn, const void* x_cal, int n, float 
                             float* scores_out, void* ws, hipStream_t stream);
 
 size_t svd_workspace_bytes(int d, int f, int r);
+// z = Q x only (the predictor's first launch), into z [r].
+hipError_t launch_svd_z(const sfn_svd& s, const void* x, float* z, hipStream_t stream);
 hipError_t launch_svd_predict(const sfn_svd& s, const void* x, int32_t* cand, int32_t* n_cand, float* p_out,
                               void* ws, hipStream_t stream);
 

@@ -193,6 +193,12 @@ size_t svd_workspace_bytes(int d, int f, int r) {
   return (bytes + 255) & ~(size_t)255;
 }
 
+hipError_t launch_svd_z(const sfn_svd& s, const void* x, float* z, hipStream_t stream) {
+  hipLaunchKernelGGL(svd_z_kernel, dim3((s.r + 1) / 2), dim3(512), 0, stream, static_cast<const char*>(s.q),
+                     static_cast<const char*>(x), s.d, s.r, z, nullptr, 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_svd_predict(const sfn_svd& s, const void* x, int32_t* cand, int32_t* n_cand, float* p_out,
                               void* ws, hipStream_t stream) {
   const int ntiles = (s.f + kRowsPerTile - 1) / kRowsPerTile;

@@ -71,6 +71,10 @@ extern "C" {
 #define SFN_ACT_SILU 0 /* SwiGLU: a = g * sigmoid(g); CATS scores |a| */
 #define SFN_ACT_RELU 1 /* ReGLU:  a = max(g, 0) */
 
+/* SVD pipelines ("SVD Contextual Sparsity Predictors for Fast LLM Inference", Table 2). */
+#define SFN_PIPE_SEQUENTIAL 0 /* gate on the candidates, then up and down where act(gate) != 0 */
+#define SFN_PIPE_PARALLEL 1   /* gate, up and down rows of every candidate in one pass */
+
 /* Limits of this build. */
 #define SFN_MAX_BATCH 4   /* tokens per sparse_ffn_decode call */
 #define SFN_MAX_CHUNK 16  /* tokens per ffn_dense_chunk call (the Sirius chunk) */
@@ -176,6 +180,32 @@ int sparse_ffn_decode_parallel(const sfn_ffn* ffn, const void* x, const int32_t*
  */
 int svd_predict(const sfn_svd* svd, const void* x, int32_t* cand_idx, int32_t* n_cand,
                 float* p_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Predictor and FFN in one call for one token, with no candidate list in between ("SVD
+ * Contextual Sparsity Predictors for Fast LLM Inference", Figures 1 and 3, Table 2):
+ * z = Q x, then each tile of rows computes p_i = L_i z + b_i for its own rows and
+ * processes its candidates {i : p_i > tau_i} directly:
+ *   SFN_PIPE_SEQUENTIAL: g_i = Wg_i x + b_gate_i on the candidates, active where
+ *     |act(g_i)| > 0 (ReLU: g_i > 0), then y = sum over active i of act(g_i) u_i Dt[i, :];
+ *     idx / n_idx: the active rows, ascending.
+ *   SFN_PIPE_PARALLEL: y = sum over candidates i of act(g_i) u_i Dt[i, :], the gate, up
+ *     and down rows read together; idx / n_idx: the candidate rows, ascending.
+ * The same result as svd_predict followed by sparse_ffn_decode (candidate mode) or
+ * sparse_ffn_decode_parallel, up to predictions that fall within rounding of tau.
+ *   ffn, svd  one layer and its predictor: bf16 weights, svd->d == ffn->d, svd->f == ffn->f
+ *   x         [d] bf16 (device)
+ *   y         [d] fp32 (device), or NULL (sequential only) for the active rows alone
+ *   idx       [f] int32 (device) or NULL, the first *n_idx entries written
+ *   n_idx     1 int32 (device) or NULL
+ * Workspace: at least sparse_ffn_svd_workspace_size(ffn, svd) bytes, 256-byte aligned,
+ * shared with the other calls like theirs. Errors: SFN_EDTYPE for fp32 weights,
+ * SFN_ESHAPE for mismatched shapes, SFN_EINVAL for a bad pipeline or nothing requested.
+ */
+size_t sparse_ffn_svd_workspace_size(const sfn_ffn* ffn, const sfn_svd* svd);
+int sparse_ffn_decode_svd(const sfn_ffn* ffn, const sfn_svd* svd, const void* x,
+                          int32_t pipeline, float* y, int32_t* idx, int32_t* n_idx,
+                          void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Dense FFN over a chunk of n tokens (1 <= n <= 16), the Sirius verification pass

@@ -149,3 +149,33 @@ def test_other_calls_validation():
     assert par(ws=None) == B.SFN_EWORKSPACE
     assert par(ws_bytes=2048) == B.SFN_EWORKSPACE
     assert pred(s=B.sfn_svd(4096, 11008, 256, 0, FAKE, FAKE, None, None)) == B.SFN_EINVAL
+
+
+@needs_lib
+def test_svd_pipeline_validation():
+    lib = B.raw()
+    ffn = _ffn(act=B.SFN_ACT_RELU)
+    svd = B.sfn_svd(4096, 11008, 256, 0, FAKE, FAKE, None, FAKE)
+    need = lib.sparse_ffn_svd_workspace_size(ctypes.byref(ffn), ctypes.byref(svd))
+    assert need > 2048 + 256 * 4
+    assert lib.sparse_ffn_svd_workspace_size(ctypes.byref(_ffn(wdtype=B.SFN_F32)), ctypes.byref(svd)) == 0
+    assert lib.sparse_ffn_svd_workspace_size(ctypes.byref(_ffn(f=11000)), ctypes.byref(svd)) == 0
+
+    def call(f=ffn, s=svd, **kw):
+        return lib.sparse_ffn_decode_svd(
+            ctypes.byref(f), ctypes.byref(s), kw.get("x", FAKE), kw.get("pipe", B.SFN_PIPE_SEQUENTIAL),
+            kw.get("y", FAKE), kw.get("idx", None), kw.get("n", None), kw.get("ws", FAKE), kw.get("ws_bytes", need),
+            None)
+    assert call(f=_ffn(wdtype=B.SFN_F32)) == B.SFN_EDTYPE
+    assert call(s=B.sfn_svd(2048, 11008, 256, 0, FAKE, FAKE, None, FAKE)) == B.SFN_ESHAPE
+    assert call(s=B.sfn_svd(4096, 11008, 256, 0, FAKE, FAKE, None, None)) == B.SFN_EINVAL
+    assert call(f=_ffn(wu=None)) == B.SFN_EINVAL
+    assert call(pipe=2) == B.SFN_EINVAL
+    assert call(pipe=B.SFN_PIPE_PARALLEL, y=None, idx=FAKE, n=FAKE) == B.SFN_EINVAL
+    assert call(y=None) == B.SFN_EINVAL  # nothing requested
+    assert call(x=None) == B.SFN_EINVAL
+    assert call(x=FAKE + 2) == B.SFN_EALIGN
+    assert call(y=FAKE + 4) == B.SFN_EALIGN
+    assert call(idx=FAKE + 2, n=FAKE) == B.SFN_EALIGN
+    assert call(ws_bytes=need - 1) == B.SFN_EWORKSPACE
+    assert call(ws=FAKE + 16) == B.SFN_EALIGN
