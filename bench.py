@@ -847,7 +847,9 @@ def predictor_quality(B, inputs, torch, ranks=(16, 32, 64, 128, 256, 512, 1024),
     zero = torch.zeros(1, dtype=torch.float32, device=dev)
     n_cal = 2 * d
     z = torch.randn((n_cal + n_eval, d), generator=gen(1_000_000 * 3 + inputs.STREAM_TAU), device=dev)
-    Rm, _ = torch.linalg.qr(torch.randn((d, d), generator=gen(1_000_000 * 3 + 999_005), device=dev))
+    # random rotation, orthogonalized on the host
+    Rm = torch.from_numpy(np.linalg.qr(np.random.default_rng(1_000_000 * 3 + 999_005).standard_normal((d, d)))[0])
+    Rm = Rm.to(device=dev, dtype=torch.float32)
     e = torch.logspace(-1.0, 1.0, d, device=dev)
     e = e * (d / e.sum())  # mean eigenvalue 1, so the gate scale is unchanged on average
     out = {"layer": "reglu d 4096 f 11008, gate rank 256 + noise", "eval_tokens": n_eval,
