@@ -619,7 +619,7 @@ def main():
     if args.summarize_traffic:
         return write_traffic(args.summarize_traffic, args.copy_probe << 20, args.command)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
     import numpy as np

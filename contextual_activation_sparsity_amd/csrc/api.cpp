@@ -92,7 +92,7 @@ const char* sparse_ffn_strerror(int status) {
     case SFN_EDTYPE: return "unsupported dtype";
     case SFN_EWORKSPACE: return "workspace missing or smaller than the size query returns";
     case SFN_EALIGN: return "pointer or row not 16-byte aligned (workspace: 256-byte)";
-    case SFN_EUNSUPPORTED: return "request not implemented by this build";
+    case SFN_EUNSUPPORTED: return "request not implemented by this library";
     case SFN_EHIP: return "HIP runtime error on launch";
     default: return "unknown status";
   }

@@ -2,7 +2,7 @@
 activity, and the recall of candidate sets.
 
 Analysis, not the decode path. "SVD Contextual Sparsity Predictors for Fast LLM
-Inference" (Figures 2, 4, 5 and 7) judges predictors by layer-wise ROC AUC and shows
+Inference" (Figures 2, 4, 5 and 7) rates predictors by layer-wise ROC AUC and shows
 that a zero threshold loses truly active neurons. Here a neuron is active for a token
 when its true gate is positive, its score is the predictor output, and a layer's AUC
 pools all (token, neuron) pairs: the probability that an active pair scores above an

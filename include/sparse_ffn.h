@@ -60,7 +60,7 @@ extern "C" {
 #define SFN_EDTYPE (-3)       /* dtype not supported by this call */
 #define SFN_EWORKSPACE (-4)   /* ws NULL or ws_bytes smaller than the query returns */
 #define SFN_EALIGN (-5)       /* a pointer or a row not 16-byte aligned */
-#define SFN_EUNSUPPORTED (-6) /* valid request this build does not implement */
+#define SFN_EUNSUPPORTED (-6) /* valid request this library does not implement */
 #define SFN_EHIP (-7)         /* the HIP runtime reported an error on launch */
 
 /* Weight (and token) dtypes. */
@@ -75,7 +75,7 @@ extern "C" {
 #define SFN_PIPE_SEQUENTIAL 0 /* gate on the candidates, then up and down where act(gate) != 0 */
 #define SFN_PIPE_PARALLEL 1   /* gate, up and down rows of every candidate in one pass */
 
-/* Limits of this build. */
+/* Limits of this library. */
 #define SFN_MAX_BATCH 4   /* tokens per sparse_ffn_decode call */
 #define SFN_MAX_CHUNK 16  /* tokens per ffn_dense_chunk call (the Sirius chunk) */
 #define SFN_MAX_D 16384

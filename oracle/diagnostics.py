@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE: see the package docstring. Imports numpy and scipy only.
 
-"SVD Contextual Sparsity Predictors for Fast LLM Inference" judges its predictors by
+"SVD Contextual Sparsity Predictors for Fast LLM Inference" rates its predictors by
 layer-wise ROC AUC (Figures 4, 5 and 7: 1 is perfect separation, 0.5 random guessing;
 the score reaches a plateau at a small rank) and shows that thresholding the prediction
 at zero misses truly active neurons (Figure 2). The pages give no formula. Readings:
