@@ -106,6 +106,15 @@ def test_ragged_shapes_f32(d, f):
     _case(w, d, f, 0.6, 4)
 
 
+@pytest.mark.parametrize("dtype_w,d,f,batch", [(1, 256, 70000, 1), (1, 256, 70000, 4), (0, 96, 700, 3),
+                                               (0, 1024, 1030, 4)])
+def test_wide_layers_and_f32_batches(dtype_w, d, f, batch):
+    """More than 65536 neurons (tiles of 256 rows; batches then fall back to the vector
+    gate, past the matrix-core gate's 1024 tiles), and fp32 batches (vector gate)."""
+    w = inputs.workload(dtype_w)
+    _case(w, d, f, 0.5, 2 * batch, batch=batch)
+
+
 @pytest.mark.parametrize("k", [0.5, 0.7])
 def test_llama2_7b_layer(k):
     w = inputs.workload(1)
