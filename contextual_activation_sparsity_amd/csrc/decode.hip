@@ -1094,11 +1094,14 @@ hipError_t launch_parallel(const DecodeArgs& a, hipStream_t s) {
 
 template <int WT>
 hipError_t dispatch_parallel(const DecodeArgs& a, hipStream_t s) {
-  // three rows per step entry: 12 weight loads in flight per thread and buffer
+  // three rows per step entry. With one chunk per thread (d up to 4096 in bf16), one row
+  // per step (6 weight loads in flight per thread over both buffers) streamed best:
+  // 27.4 / 16.4 / 10.9 us per call at 50 / 20 / 5% candidates of f 11008, against 29.1 /
+  // 18.7 / 11.8 with four rows
   if (a.nch > 2048) return hipErrorInvalidValue;
   if (a.nch > 1024) return launch_parallel<WT, 4, 512, 1>(a, s);
   if (a.nch > 512) return launch_parallel<WT, 2, 512, 2>(a, s);
-  if (a.nch > 256) return launch_parallel<WT, 1, 512, 4>(a, s);
+  if (a.nch > 256) return launch_parallel<WT, 1, 512, 1>(a, s);
   if (a.nch > 128) return launch_parallel<WT, 1, 256, 4>(a, s);
   if (a.nch > 64) return launch_parallel<WT, 1, 128, 4>(a, s);
   return launch_parallel<WT, 1, 64, 2>(a, s);
@@ -1107,13 +1110,17 @@ hipError_t dispatch_parallel(const DecodeArgs& a, hipStream_t s) {
 template <int WT, int BMAX>
 hipError_t dispatch_tpr(const DecodeArgs& a, hipStream_t s) {
   // rows per thread per half step: 16 weight loads in flight per thread and buffer for
-  // one token, 8 for four tokens (the dot-product registers grow with the batch)
+  // one token, 8 for four tokens (the dot-product registers grow with the batch). With
+  // one chunk per thread (d up to 4096 in bf16) 2 rows stream faster, i.e. 8 loads in
+  // flight per thread over both buffers for one token: 39.8-41.1 against 43.3-44.4 us
+  // per call at d 4096, f 11008, and 47.2 against 51.7 us at f 14336 (batches of two:
+  // 63.8 against 64.7 us at f 14336; four tokens unchanged).
   constexpr int RB = BMAX == 1 ? 8 : 4;
-  constexpr int RG1 = RB;
+  constexpr int R1 = 2;
   if (a.nch > 2048) return hipErrorInvalidValue;
   if (a.nch > 1024) return launch_pair<WT, BMAX, 4, 512, RB / 4, RB / 4>(a, s);
   if (a.nch > 512) return launch_pair<WT, BMAX, 2, 512, RB / 2, RB / 2>(a, s);
-  if (a.nch > 256) return launch_pair<WT, BMAX, 1, 512, RG1, RB>(a, s);
+  if (a.nch > 256) return launch_pair<WT, BMAX, 1, 512, R1, R1>(a, s);
   if (a.nch > 128) return launch_pair<WT, BMAX, 1, 256, RB, RB>(a, s);
   if (a.nch > 64) return launch_pair<WT, BMAX, 1, 128, RB, RB>(a, s);
   return launch_pair<WT, BMAX, 1, 64, 4, 4>(a, s);
