@@ -72,3 +72,27 @@ def mask_from_idx(idx, n, f):
     m = np.zeros(f, dtype=bool)
     m[np.asarray(idx[:n], dtype=np.int64)] = True
     return m
+
+
+_REGLU_SVD_CACHE = {}
+
+
+def reglu_svd_layer(d, f, r, rank_struct=256):
+    """The ReGLU workload's layer 0 at shape (d, f) with the oracle's rank-r factors,
+    rounded to bf16: (raw layer, Wg float64, b float64, Q bits, L bits, Q float64,
+    L float64). Computed once per shape and rank in a test session: the float64 SVD of a
+    4096 x 11008 gate takes seconds, and several tests use the same one."""
+    key = (d, f, r, rank_struct)
+    if key not in _REGLU_SVD_CACHE:
+        w = inputs.workload(3)
+        raw = inputs.reglu_layer(w, 0, d=d, f=f, rank_struct=rank_struct)
+        Wg = to_f64(raw["w_gate"], "bf16")
+        b = raw["b_gate"].astype(np.float64)
+        Q, L = oracle.svd_factors(Wg, r)
+        Qb, Lb = inputs.f32_to_bf16_bits(Q), inputs.f32_to_bf16_bits(L)
+        while len(_REGLU_SVD_CACHE) >= 4:  # a few layers, under a few GB of float64
+            _REGLU_SVD_CACHE.pop(next(iter(_REGLU_SVD_CACHE)))
+        _REGLU_SVD_CACHE[key] = (raw, Wg, b, Qb, Lb, to_f64(Qb, "bf16"), to_f64(Lb, "bf16"))
+    else:
+        _REGLU_SVD_CACHE[key] = _REGLU_SVD_CACHE.pop(key)  # most recently used last
+    return _REGLU_SVD_CACHE[key]

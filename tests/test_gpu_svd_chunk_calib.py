@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from contextual_activation_sparsity_amd import inputs
-from tests.helpers import (TOL_BF16, TOL_F32, check_mask, mask_from_idx, normwise_err, say,
+from tests.helpers import (TOL_BF16, TOL_F32, check_mask, mask_from_idx, normwise_err, reglu_svd_layer, say,
                            swiglu_layer_dev, to_dev, to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -19,12 +19,7 @@ if torch.cuda.is_available():
 def _svd_case(d, f, r, s, n_tok, n_cal=256, rank_struct=256):
     w = inputs.workload(3)
     say(f"[svd] d={d} f={f} r={r} s={s}")
-    raw = inputs.reglu_layer(w, 0, d=d, f=f, rank_struct=rank_struct)
-    Wg = to_f64(raw["w_gate"], "bf16")
-    b = raw["b_gate"].astype(np.float64)
-    Q, L = oracle.svd_factors(Wg, r)
-    Qb, Lb = inputs.f32_to_bf16_bits(Q), inputs.f32_to_bf16_bits(L)
-    Q64, L64 = to_f64(Qb, "bf16"), to_f64(Lb, "bf16")
+    raw, Wg, b, Qb, Lb, Q64, L64 = reglu_svd_layer(d, f, r, rank_struct)
     xcal = to_f64(inputs.tokens(w, n_cal, inputs.STREAM_TAU, d=d), "bf16")
     P = np.array([oracle.svd_predict(Q64, L64, xc, b) for xc in xcal])
     G = xcal @ Wg.T + b

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from contextual_activation_sparsity_amd import inputs
-from tests.helpers import TOL_BF16, mask_from_idx, normwise_err, say, to_dev, to_f64
+from tests.helpers import TOL_BF16, mask_from_idx, normwise_err, reglu_svd_layer, say, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -27,12 +27,8 @@ BAND = 1e-3
 
 def _setup(d, f, r, s=0.5, act="relu", tau_override=None):
     w = inputs.workload(3)
-    raw = inputs.reglu_layer(w, 0, d=d, f=f, rank_struct=min(256, d, f))
-    Wg, Wu, Dt = (to_f64(raw[k], "bf16") for k in ("w_gate", "w_up", "w_down_t"))
-    b = raw["b_gate"].astype(np.float64)
-    Q, L = oracle.svd_factors(Wg, r)
-    Qb, Lb = inputs.f32_to_bf16_bits(Q), inputs.f32_to_bf16_bits(L)
-    Q64, L64 = to_f64(Qb, "bf16"), to_f64(Lb, "bf16")
+    raw, Wg, b, Qb, Lb, Q64, L64 = reglu_svd_layer(d, f, r, min(256, d, f))
+    Wu, Dt = (to_f64(raw[k], "bf16") for k in ("w_up", "w_down_t"))
     if tau_override is None:
         xcal = to_f64(inputs.tokens(w, 512, inputs.STREAM_TAU, d=d), "bf16")
         P = (xcal @ Q64.T) @ L64.T + b
