@@ -15,8 +15,11 @@
 // and a per-wave LDS hand-off. Wave 0 turns the sums into activations, applies the
 // threshold and compacts the active rows with ballot + mbcnt, in ascending order, into
 // the tile's slice of a global list (row, activations, per-token bits) plus a count.
+// Batches of 2 to 4 tokens with bf16 weights take a matrix-core gate over 16-row tiles
+// instead (decode_gate_mfma_kernel), with the same outputs. In predict mode each tile
+// first runs the SVD predictor on its own rows and gates its candidates (predict_tile).
 //
-// Launch 2, up/down kernel (G workgroups): the active lists of all tiles form one
+// Launch 2, up/down kernel (Gu workgroups): the active lists of all tiles form one
 // concatenated list; each workgroup takes an equal share of it (a prefix over the tile
 // counts in LDS), gathers the Wu and Dt rows of its share (each one contiguous row, Dt
 // being W_down transposed), reduces u = Wu x like the gate, forms h = m a u and
@@ -33,6 +36,9 @@
 // a fixed order, so y is deterministic; its first workgroup also assembles the
 // per-token active index lists. The kernel boundary orders the partial stores before
 // the loads: no device-scope atomics, fences or waits anywhere in the decode path.
+//
+// The one-pass kernel (parallel pipeline of the SVD predictor) reads the gate, up and
+// down rows of each candidate together and ends in the same reduce kernel.
 
 #include "device_common.h"
 #include "kernels.h"

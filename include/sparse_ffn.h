@@ -13,7 +13,9 @@
  *   - SVD predictor ("SVD Contextual Sparsity Predictors for Fast LLM Inference",
  *     abstract, Figures 1 and 3): a rank-r predictor p = L (Q x) + b with per-neuron
  *     thresholds tau picks candidate rows; the gate is evaluated on the candidates only
- *     and up/down only where ReLU(gate) > 0 (the sequential pipeline);
+ *     and up/down only where ReLU(gate) > 0 (the sequential pipeline), or the gate, up
+ *     and down rows of every candidate are read in one pass (the parallel pipeline,
+ *     Table 2);
  *   - Sirius ("SIRIUS: Contexual Sparisty with Correction for Efficient LLMs",
  *     Approach): the full model re-runs a chunk of up to 16 tokens densely with the same
  *     weights to verify them.
