@@ -51,10 +51,16 @@ def log(msg):
 
 
 def kernel_hash():
+    """Hash of the decode kernels' code: the sources with comments and blank space
+    removed, so that a change to a comment does not invalidate the counter summary."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, rel)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
