@@ -300,3 +300,11 @@ def test_one_workspace_shared_by_every_call():
     say("[shared ws] calibrate again, decode")
     B.sparse_ffn_calibrate(layer, to_dev(xcal_raw, "bf16"), 0.7, t_dev, ws)
     decode_check(2)
+
+
+@pytest.mark.parametrize("d,f,batch", [(16384, 600, 1), (16384, 600, 4), (64, 262144, 1), (64, 262144, 3)])
+def test_limits(d, f, batch):
+    """The largest rows (d 16384: four 16-byte chunks per thread) and the most neurons
+    (f 262144: 1024 tiles of 256 rows, the most a launch takes)."""
+    w = inputs.workload(1)
+    _case(w, d, f, 0.5, batch, batch=batch)

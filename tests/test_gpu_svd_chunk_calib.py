@@ -119,7 +119,8 @@ def test_svd_parallel_pipeline_end_to_end():
 
 @pytest.mark.parametrize("wi,d,f,act,frac", [(1, 4096, 11008, "silu", 0.3), (1, 1024, 3000, "relu", 0.5),
                                               (1, 8192, 2048, "silu", 0.2), (0, 256, 688, "silu", 0.4),
-                                              (1, 2048, 700, "relu", 0.0), (5, 3584, 18944, "silu", 0.05)])
+                                              (1, 2048, 700, "relu", 0.0), (5, 3584, 18944, "silu", 0.05),
+                                              (1, 16384, 600, "silu", 0.4)])
 def test_parallel_candidate_lists(wi, d, f, act, frac):
     """Unsorted candidate lists of a given fraction of the rows (empty at 0): y is the
     FFN masked to those rows, act(g) u summed against Dt, as the oracle computes it."""
@@ -153,7 +154,8 @@ def test_parallel_candidate_lists(wi, d, f, act, frac):
 
 # ---------------------------------------------------------------------------- chunk
 @pytest.mark.parametrize("d,f,n", [(4096, 11008, 16), (1024, 3000, 5), (512, 1001, 1), (8192, 2048, 16),
-                                   (2048, 4100, 9), (8192, 28672, 16), (4096, 11008, 1), (3584, 18944, 1)])
+                                   (2048, 4100, 9), (8192, 28672, 16), (4096, 11008, 1), (3584, 18944, 1),
+                                   (16384, 300, 16)])
 def test_dense_chunk_bf16(d, f, n):
     w = inputs.workload(4)
     say(f"[chunk] d={d} f={f} n={n}")
