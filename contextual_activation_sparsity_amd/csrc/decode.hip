@@ -33,9 +33,10 @@
 //
 // End of launch 2: each workgroup writes its fp32 partial of y with plain vector stores.
 // Launch 3, reduce kernel: y = the sum of the partials, column slice by column slice, in
-// a fixed order, so y is deterministic; its first workgroup also assembles the
-// per-token active index lists. The kernel boundary orders the partial stores before
-// the loads: no device-scope atomics, fences or waits anywhere in the decode path.
+// a fixed order, so y is deterministic; its workgroups also assemble the per-token
+// active index lists, each the slices of a share of the gate tiles. The kernel boundary
+// orders the partial stores before the loads: no device-scope atomics, fences or waits
+// anywhere in the decode path.
 //
 // The one-pass kernel (parallel pipeline of the SVD predictor) reads the gate, up and
 // down rows of each candidate together and ends in the same reduce kernel.
@@ -950,7 +951,7 @@ struct ParKernel {
 // y = sum of the partials of the up/down kernel, in chunks of 32 columns (128 bytes of
 // each partial row): lane l of group g sums column l of partials g, g + 16, g + 32, ...
 // (16 loads in flight), then group 0 adds the 16 group sums in order, so y is
-// deterministic. Workgroup 0 also assembles the per-token active index lists.
+// deterministic. The workgroups also assemble the per-token active index lists.
 constexpr int kRedCols = 32;
 constexpr int kRedGroups = 16;
 
@@ -998,7 +999,7 @@ struct ReduceKernel {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ri = blockIdx.x;
     const int nb = a.nb;
-    if (a.y) {
+    if (a.y && ri < a.n_red) {
       const int L = nb * a.d;
       const int nck = (L + kRedCols - 1) / kRedCols;
       const int c0 = share_begin(ri, nck, a.n_red), c1 = share_begin(ri + 1, nck, a.n_red);
@@ -1028,22 +1029,24 @@ struct ReduceKernel {
         __syncthreads();
       }
     }
-    const bool want_idx = a.active_idx != nullptr || a.n_active != nullptr;
-    if (want_idx && ri == 0) {
-      // per-token active rows, ascending: concatenate the tiles' lists
+    // per-token active rows, ascending: the tiles' slices concatenated. Every workgroup
+    // forms the prefix over all tile counts and copies the slices of its own share of the
+    // tiles (one tile per wave); workgroup 0 writes the counts.
+    const int nw = gridDim.x;
+    const int t0 = a.active_idx ? share_begin(ri, a.G, nw) : 0;
+    const int t1 = a.active_idx ? share_begin(ri + 1, a.G, nw) : 0;
+    if (t0 < t1 || (ri == 0 && a.n_active)) {
       const int n_total = a.cand ? min(max(*a.n_cand, 0), a.f) : a.f;
       for (int b = 0; b < nb; ++b) {
         __syncthreads();
         tile_prefix(a, sm, 1 + b);
-        if (a.active_idx) {
-          for (int tile = wave; tile < a.G; tile += kRT / 64) {
-            const int tr0 = share_begin(tile, n_total, a.G);
-            const int c = sm.pref[tile + 1] - sm.pref[tile];
-            for (int i = lane; i < c; i += 64)
-              a.active_idx[(size_t)b * a.f + sm.pref[tile] + i] = a.tile_idx[(size_t)b * a.f + tr0 + i];
-          }
+        for (int tile = t0 + wave; tile < t1; tile += kRT / 64) {
+          const int tr0 = share_begin(tile, n_total, a.G);
+          const int c = sm.pref[tile + 1] - sm.pref[tile];
+          for (int i = lane; i < c; i += 64)
+            a.active_idx[(size_t)b * a.f + sm.pref[tile] + i] = a.tile_idx[(size_t)b * a.f + tr0 + i];
         }
-        if (tid == 0 && a.n_active) a.n_active[b] = sm.pref[a.G];
+        if (ri == 0 && tid == 0 && a.n_active) a.n_active[b] = sm.pref[a.G];
       }
     }
   }
@@ -1060,6 +1063,15 @@ __global__ __launch_bounds__(kNT) void decode_updown_kernel(DecodeArgs a) {
 }
 
 __global__ __launch_bounds__(512) void decode_reduce_kernel(DecodeArgs a, int P) { ReduceKernel::run(a, P); }
+
+// Workgroups of the reduce kernel: the column chunks of y (n_red), and when the index
+// lists are asked for, at least one workgroup per four gate tiles (G is the gate's tile
+// count, which for the matrix-core gate differs from the up/down grid).
+int reduce_grid(const DecodeArgs& g) {
+  int n = g.y ? g.n_red : 1;
+  if (g.active_idx && (g.G + 3) / 4 > n) n = (g.G + 3) / 4;
+  return n;
+}
 
 // Batches of at least this many tokens take the matrix-core gate (bf16 weights, at most
 // kGMax tiles of 16 rows, no candidate list): its cost per row does not grow with the batch.
@@ -1081,7 +1093,7 @@ hipError_t launch_pair(const DecodeArgs& a, hipStream_t s) {
   }
   if (a.y) hipLaunchKernelGGL((decode_updown_kernel<WT, BMAX, CPT, TPR, RUP>), dim3(g.Gu), dim3(kNT), 0, s, g);
   if (a.y || a.active_idx || a.n_active)
-    hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.y ? a.n_red : 1), dim3(ReduceKernel::kRT), 0, s, g,
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3(reduce_grid(g)), dim3(ReduceKernel::kRT), 0, s, g,
                        g.Gu * (kNT / TPR));
   return hipGetLastError();
 }
@@ -1094,7 +1106,8 @@ __global__ __launch_bounds__(kNT) void decode_parallel_kernel(DecodeArgs a) {
 template <int WT, int CPT, int TPR, int R>
 hipError_t launch_parallel(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((decode_parallel_kernel<WT, CPT, TPR, R>), dim3(a.G), dim3(kNT), 0, s, a);
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.n_red), dim3(ReduceKernel::kRT), 0, s, a, a.G * (kNT / TPR));
+  hipLaunchKernelGGL(decode_reduce_kernel, dim3(reduce_grid(a)), dim3(ReduceKernel::kRT), 0, s, a,
+                     a.G * (kNT / TPR));
   return hipGetLastError();
 }
 
