@@ -8,15 +8,15 @@ thresholds are calibrated per layer by the library (256 calibration tokens) for 
 headline sparsity (50%) and for the sweep points (70/80/90%).
 
 A step is one decode token through all 32 layers (32 sparse_ffn_decode calls; each call
-is three kernels: gate, up/down, reduce). After W untimed warm-up steps, K steps are
+is two kernels: gate with each tile's up/down, then the reduce). After W untimed warm-up steps, K steps are
 timed with HIP events on the stream the kernels run on (graph mode: one captured graph
 per token, replayed back to back). The JSON line on stdout carries:
   value      decode tokens/s at the headline sparsity (inputs resident in HBM)
   roofline   one sparse_ffn_decode call: algorithmic bytes per call (all gate rows, the
              active up and down rows, x and y) over the average call duration in the
              timed region, against the 8 TB/s HBM peak; `stages` splits the call into
-             the gate kernel (timed alone, from calls that request no output) and the
-             rest; `traffic` is the HBM bytes per call from the committed rocprofv3
+             the gate (the gate kernel timed alone, from calls that request no output)
+             and the rest; `traffic` is the HBM bytes per call from the committed rocprofv3
              counter summary, when that summary was taken on the current kernel source
   cpu_baseline  the CPU oracle (dense FFN then mask, numpy float64) timed on a bounded
              sample of layers and tokens of the same workload on this host
@@ -90,7 +90,9 @@ def parse():
     return ap.parse_args()
 
 
-DECODE_KERNELS = ("decode_gate_kernel", "decode_updown_kernel", "decode_reduce_kernel")
+DECODE_KERNELS = ("decode_gate_local_kernel", "decode_gate_kernel", "decode_updown_kernel", "decode_reduce_kernel")
+# the kernels of one batch-1 decode call (the gate kernel alone runs in the gate-only timing)
+CALL_KERNELS = ("decode_gate_local_kernel", "decode_reduce_kernel")
 COPY_KERNEL = "copy_kernel"
 
 
@@ -693,12 +695,12 @@ def main():
             traffic = tr.get("bytes_per_call")
     roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                "kernel": "sparse_ffn_decode call (decode_gate_kernel + decode_updown_kernel + decode_reduce_kernel), "
+                "kernel": "sparse_ffn_decode call (decode_gate_local_kernel + decode_reduce_kernel), "
                           "bf16, batch 1, d 4096, f 11008",
                 "algorithmic_bytes_per_launch": per_call_bytes, "avg_launch_us": call_us, "launches": K * L,
                 "stages": {"gate_kernel": {"us": gate_us, "bytes": gate_bytes,
                                            "gbs": gate_bytes / (gate_us * 1e-6) / 1e9},
-                           "updown_and_reduce_kernels": {"us": call_us - gate_us, "bytes": per_call_bytes - gate_bytes,
+                           "updown_and_reduce": {"us": call_us - gate_us, "bytes": per_call_bytes - gate_bytes,
                                                          "gbs": (per_call_bytes - gate_bytes)
                                                          / ((call_us - gate_us) * 1e-6) / 1e9}}}
     log(f"  decode call: {call_us:.2f} us, {achieved:.1f} GB/s algorithmic ({achieved / PEAK_HBM_GBS:.3f}); "
@@ -910,9 +912,9 @@ def predictor_quality(B, inputs, torch, ranks=(16, 32, 64, 128, 256, 512, 1024),
 
 
 def write_traffic(dirs, probe, command):
-    """HBM bytes per decode call: FETCH_SIZE and WRITE_SIZE of the three decode kernels,
-    each counter scaled so that the probe's copy of `probe` bytes reads (writes) exactly
-    `probe` bytes."""
+    """HBM bytes per decode call: FETCH_SIZE and WRITE_SIZE of the kernels of a batch-1
+    decode call, each counter scaled so that the probe's copy of `probe` bytes reads
+    (writes) exactly `probe` bytes."""
     if probe <= 0:
         raise SystemExit("--copy-probe MIB must give the probe's size")
     res = summarize_traffic(dirs[0], dirs[1], probe)
@@ -920,13 +922,13 @@ def write_traffic(dirs, probe, command):
     detail = {}
     for counter, r in res.items():
         scale = probe / r["copy_probe_bytes_counted"]
-        ks = {k: v * scale for k, v in r["per_kernel_bytes"].items() if k in DECODE_KERNELS}
+        ks = {k: v * scale for k, v in r["per_kernel_bytes"].items() if k in CALL_KERNELS}
         detail[counter] = {"scale": scale, "probe_counted_bytes": r["copy_probe_bytes_counted"],
                            "per_kernel_bytes": ks}
         per_call += sum(ks.values())
     out = {"kernel_hash": kernel_hash(), "bytes_per_call": per_call, "counters": detail, "command": command,
-           "note": "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median over dispatches) of the three decode "
-                   "kernels, summed; each counter scaled by probe bytes / what it reads for a plain elementwise "
+           "note": "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median over dispatches) of the kernels of "
+                   "a batch-1 decode call, summed; each counter scaled by probe bytes / what it reads for a plain elementwise "
                    "copy (torch.neg) of 1 GiB in the same run. kernel_hash covers the decode kernel sources."}
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)

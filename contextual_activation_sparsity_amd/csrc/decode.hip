@@ -1,4 +1,4 @@
-// Sparse gated-FFN decode step: three launches per layer.
+// Sparse gated-FFN decode step: two launches per layer for one token, three for a batch.
 //
 // What it computes (for each token b of the batch):
 //   g = Wg x_b + bias, a = act(g), m_bi = [|a_i| > t] (or the mask override, or the
@@ -8,32 +8,36 @@
 // Contextual Sparsity Predictors for Fast LLM Inference" (Figure 3: gate on the
 // predicted rows, up and down only where ReLU(gate) > 0).
 //
-// Launch 1, gate kernel (G workgroups of 512 threads, one tile of rows each, or an equal
-// share of the candidate list): streams the gate rows. Thread t of a row reads 16-byte
-// chunk t, so a 4096-wide bf16 row is one coalesced 8 KB sweep of the workgroup; partial
-// dot products are reduced with a multi-value transposing butterfly (DPP + swizzles)
-// and a per-wave LDS hand-off. Wave 0 turns the sums into activations, applies the
-// threshold and compacts the active rows with ballot + mbcnt, in ascending order, into
-// the tile's slice of a global list (row, activations, per-token bits) plus a count.
-// Batches of 2 to 4 tokens with bf16 weights take a matrix-core gate over 16-row tiles
-// instead (decode_gate_mfma_kernel), with the same outputs. In predict mode each tile
-// first runs the SVD predictor on its own rows and gates its candidates (predict_tile).
+// Gate (G workgroups of 512 threads, one tile of rows each, or an equal share of the
+// candidate list): streams the gate rows. Thread t of a row reads 16-byte chunk t, so a
+// 4096-wide bf16 row is one coalesced 8 KB sweep of the workgroup; partial dot products
+// are reduced with a multi-value transposing butterfly (DPP + swizzles) and a per-wave
+// LDS hand-off. Wave 0 turns the sums into activations, applies the threshold and
+// compacts the active rows with ballot + mbcnt, in ascending order, into the tile's
+// slice of a global list (row, activations, per-token bits) plus a count. Batches of 2
+// to 4 tokens with bf16 weights take a matrix-core gate over 16-row tiles instead
+// (decode_gate_mfma_kernel), with the same outputs. In predict mode each tile first runs
+// the SVD predictor on its own rows and gates its candidates (predict_tile).
 //
-// Launch 2, up/down kernel (Gu workgroups): the active lists of all tiles form one
-// concatenated list; each workgroup takes an equal share of it (a prefix over the tile
-// counts in LDS), gathers the Wu and Dt rows of its share (each one contiguous row, Dt
-// being W_down transposed), reduces u = Wu x like the gate, forms h = m a u and
-// accumulates h * Dt into fp32 registers for the columns of its chunk. Splitting the list
-// evenly keeps every workgroup's share within one row of the mean, where a per-tile split
-// would follow the binomial spread of the active counts.
+// Up/down: gathers the Wu and Dt rows of a list of active rows (each one contiguous row,
+// Dt being W_down transposed), reduces u = Wu x like the gate, forms h = m a u and
+// accumulates h * Dt into fp32 registers for the columns of its chunk, then writes the
+// workgroup's fp32 partial of y with plain vector stores.
+//  * One token (decode_gate_local_kernel, launch 1 of 2): the workgroup that gated a
+//    tile streams the up/down rows of that tile's active rows right after, from a copy of
+//    the list in LDS. A tile's share follows the spread of its active count, but the
+//    separate launch, its scan over the tile counts and its gather of a share cost more.
+//  * Batches (decode_updown_kernel, launch 2 of 3): the active lists of all tiles form one
+//    concatenated list and each of Gu workgroups takes an equal share of it (a prefix over
+//    the tile counts in LDS): the union rows of several tokens are many, and an even split
+//    keeps every share within one row of the mean.
 //
-// In both kernels the loads of the next step are in flight while the current step is
-// reduced (the issue sequence is the same for every kind of step, so the compiler's wait
-// counts cover exactly the older buffer).
+// In the streaming loops the loads of the next step are in flight while the current step
+// is reduced (the issue sequence is the same for every kind of step, so the compiler's
+// wait counts cover exactly the older buffer).
 //
-// End of launch 2: each workgroup writes its fp32 partial of y with plain vector stores.
-// Launch 3, reduce kernel: y = the sum of the partials, column slice by column slice, in
-// a fixed order, so y is deterministic; its workgroups also assemble the per-token
+// Last launch, reduce kernel: y = the sum of the partials, column slice by column slice,
+// in a fixed order, so y is deterministic; its workgroups also assemble the per-token
 // active index lists, each the slices of a share of the gate tiles. The kernel boundary
 // orders the partial stores before the loads: no device-scope atomics, fences or waits
 // anywhere in the decode path.
@@ -316,7 +320,10 @@ struct GateKernel {
     }
   }
 
-  __device__ static void run(const DecodeArgs& args) {
+  // rec(slot, row, activations, bits) is called by wave 0 for every selected row, slot
+  // being its position in the tile's slice; returns the tile's selected-row count.
+  template <class Rec>
+  __device__ static int run(const DecodeArgs& args, Rec&& rec) {
     const DevArgs a = dev_args(args);
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -402,6 +409,7 @@ struct GateKernel {
 #pragma unroll
           for (int b = 0; b < BMAX; ++b)
             if (b < nb) a.sel_a[(size_t)b * a.f + o] = av[b];
+          rec(q0 + pos, grow, av, bits);
         }
         if (want_idx) {
 #pragma unroll
@@ -451,6 +459,7 @@ struct GateKernel {
       else if (tid - 1 < BMAX) v = sm.cnt[tid - 1];
       a.tile_cnt[w * kCnt + tid] = v;
     }
+    return sm.qlen;
   }
 };
 
@@ -638,20 +647,11 @@ struct UpDownKernel {
     const DevArgs a = dev_args(args);
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rl = tid / TPR, cl = tid % TPR;
     const int w = blockIdx.x;
     const bool cand_mode = a.cand != nullptr;
     const bool want_y = a.y != nullptr;
     const int nb = a.nb;
     const int n_total = cand_mode ? min(max(*a.n_cand, 0), a.f) : a.f;  // rows the gate tiles cover
-
-    float acc[BMAX][CPT][KV];
-#pragma unroll
-    for (int b = 0; b < BMAX; ++b)
-#pragma unroll
-      for (int c = 0; c < CPT; ++c)
-#pragma unroll
-        for (int v = 0; v < KV; ++v) acc[b][c][v] = 0.f;
 
     if (want_y) {
       // ---- this workgroup's equal share [s0, s0 + nq) of the concatenated active lists.
@@ -700,6 +700,24 @@ struct UpDownKernel {
 #pragma unroll
         for (int b = 0; b < BMAX; ++b) sm.qa[j][b] = b < nb ? a.sel_a[(size_t)b * a.f + o] : 0.f;
       }
+      stream(a, sm, nq, w);
+    }
+  }
+
+  // Up and down rows of share entries [0, nq) (rows, activations and bits in sm), then
+  // the workgroup's partial of y in partial rows w RPG .. w RPG + RPG - 1.
+  __device__ static void stream(const DevArgs& a, Smem& sm, int nq, int w) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rl = tid / TPR, cl = tid % TPR;
+    const int nb = a.nb;
+    float acc[BMAX][CPT][KV];
+#pragma unroll
+    for (int b = 0; b < BMAX; ++b)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c)
+#pragma unroll
+        for (int v = 0; v < KV; ++v) acc[b][c][v] = 0.f;
+    {
       uint4 xr[BMAX][CPT];
       S::load_x(a, cl, xr);
       __syncthreads();
@@ -1054,7 +1072,29 @@ struct ReduceKernel {
 
 template <int WT, int BMAX, int CPT, int TPR, int R>
 __global__ __launch_bounds__(kNT) void decode_gate_kernel(DecodeArgs a) {
-  GateKernel<WT, BMAX, CPT, TPR, R>::run(a);
+  GateKernel<WT, BMAX, CPT, TPR, R>::run(a, [](int, int, const auto&, uint32_t) {});
+}
+
+// Gate and up/down of one tile in one workgroup: the tile's selected rows are recorded
+// in LDS as the gate finds them, and the same workgroup then streams their up and down
+// rows and writes its partial of y. No list crosses workgroups, so the up/down launch
+// and its prologue (a scan over the tile counts, then a gather of the share) disappear;
+// the price is that a tile's share follows the spread of its selected-row count. One
+// token at d 4096: 37.1-37.3 against 40.4 us per call at f 11008 and 50% sparsity, 29.8
+// against 33.4 at 80%, 46.1 against 50.1 at f 14336; 156.6 against 160.8 at d 8192,
+// f 28672. Both 1.5x and 2x the tiles, and 1 or 4 up/down rows per step, were slower.
+template <int WT, int BMAX, int CPT, int TPR, int RGATE, int RUP>
+__global__ __launch_bounds__(kNT) void decode_gate_local_kernel(DecodeArgs args) {
+  using UD = UpDownKernel<WT, BMAX, CPT, TPR, RUP>;
+  __shared__ typename UD::Smem usm;
+  const int n = GateKernel<WT, BMAX, CPT, TPR, RGATE>::run(
+      args, [&](int slot, int row, const auto& av, uint32_t bits) {
+        usm.qrow[slot] = row;
+        usm.qbits[slot] = (uint8_t)bits;
+#pragma unroll
+        for (int b = 0; b < BMAX; ++b) usm.qa[slot][b] = av[b];
+      });
+  UD::stream(dev_args(args), usm, n, blockIdx.x);
 }
 
 template <int WT, int BMAX, int CPT, int TPR, int R>
@@ -1085,13 +1125,19 @@ hipError_t launch_pair(const DecodeArgs& a, hipStream_t s) {
   DecodeArgs g = a;  // gate tiles G, up/down workgroups Gu
   g.Gu = a.G;
   const bool mfma = WT == WT_BF16 && !a.cand && !a.pl && a.nb >= kMfmaGateMinBatch && mfma_gate_tiles(a.f) <= kGMax;
+  // one token: each tile streams the up/down rows of its own selected rows
+  const bool local = BMAX == 1 && a.y;
   if (mfma) {
     g.G = mfma_gate_tiles(a.f);
     hipLaunchKernelGGL((decode_gate_mfma_kernel<BMAX>), dim3(g.G), dim3(256), 0, s, g);
+  } else if (local) {
+    if constexpr (BMAX == 1)
+      hipLaunchKernelGGL((decode_gate_local_kernel<WT, BMAX, CPT, TPR, RGATE, RUP>), dim3(g.G), dim3(kNT), 0, s, g);
   } else {
     hipLaunchKernelGGL((decode_gate_kernel<WT, BMAX, CPT, TPR, RGATE>), dim3(g.G), dim3(kNT), 0, s, g);
   }
-  if (a.y) hipLaunchKernelGGL((decode_updown_kernel<WT, BMAX, CPT, TPR, RUP>), dim3(g.Gu), dim3(kNT), 0, s, g);
+  if constexpr (BMAX > 1)
+    if (a.y) hipLaunchKernelGGL((decode_updown_kernel<WT, BMAX, CPT, TPR, RUP>), dim3(g.Gu), dim3(kNT), 0, s, g);
   if (a.y || a.active_idx || a.n_active)
     hipLaunchKernelGGL(decode_reduce_kernel, dim3(reduce_grid(g)), dim3(ReduceKernel::kRT), 0, s, g,
                        g.Gu * (kNT / TPR));

@@ -49,11 +49,12 @@ struct DecodeArgs {
   int d, f, nch, row_bytes, nb, act, G, n_red, Gu;
 };
 
-// Decode (three launches per call: a gate kernel over tiles of rows that writes compacted
-// active lists, an up/down kernel that splits the concatenated list evenly and writes
-// fp32 partials of y, and a reduce kernel that sums them in a fixed order):
-// workgroups per launch for f neurons, reducing workgroups, rows a workgroup handles
-// side by side (partials per workgroup), workspace bytes, carving of the workspace.
+// Decode (a gate kernel over tiles of rows that writes compacted active lists; for one
+// token each tile then streams the up/down rows of its own active rows, for a batch an
+// up/down kernel splits the concatenated list evenly; both write fp32 partials of y, and
+// a reduce kernel sums them in a fixed order): workgroups per launch for f neurons,
+// reducing workgroups, rows a workgroup handles side by side (partials per workgroup),
+// workspace bytes, carving of the workspace.
 int decode_grid(int f);
 int decode_reducers(int G, int nb, int d);
 int decode_rows_side_by_side(int nch);
