@@ -88,6 +88,7 @@ struct DevArgs {
   SFN_GLOBAL float* sel_a;
   SFN_GLOBAL uint8_t* sel_bits;
   SFN_GLOBAL float* part;
+  SFN_GLOBAL uint32_t* flags;
   const SFN_GLOBAL char* pl;
   const SFN_GLOBAL float* pz;
   const SFN_GLOBAL float* ptau;
@@ -102,7 +103,7 @@ __device__ __forceinline__ DevArgs dev_args(const DecodeArgs& h) {
   a.cand = gp(h.cand); a.n_cand = gp(h.n_cand); a.mask_in = gp(h.mask_in); a.y = gp(h.y);
   a.active_idx = gp(h.active_idx); a.n_active = gp(h.n_active);
   a.tile_cnt = gp(h.tile_cnt); a.tile_idx = gp(h.tile_idx); a.sel_idx = gp(h.sel_idx); a.sel_a = gp(h.sel_a);
-  a.sel_bits = gp(h.sel_bits); a.part = gp(h.part);
+  a.sel_bits = gp(h.sel_bits); a.part = gp(h.part); a.flags = gp(h.flags);
   a.pl = gp(h.pl); a.pz = gp(h.pz); a.ptau = gp(h.ptau); a.pb = gp(h.pb); a.pr = h.pr;
   a.d = h.d; a.f = h.f; a.nch = h.nch; a.row_bytes = h.row_bytes; a.nb = h.nb; a.act = h.act; a.G = h.G;
   a.n_red = h.n_red;
@@ -117,6 +118,17 @@ __device__ __attribute__((aligned(16))) uint8_t g_zero_u8[16];
 
 // First entry of share w when n entries are split over G workgroups.
 __device__ __forceinline__ int share_begin(int w, int n, int G) { return (int)((long long)w * n / G); }
+
+// Words other workgroups read during the same launch: relaxed device-scope atomics,
+// which go through to memory past this XCD's L2 (the L2s of the eight XCDs are not
+// coherent with each other) without the whole-L2 writeback or invalidation that a
+// release or acquire fence would cost.
+__device__ __forceinline__ void st_through(SFN_GLOBAL uint32_t* p, uint32_t v) {
+  __hip_atomic_store((uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_through(const SFN_GLOBAL uint32_t* p) {
+  return __hip_atomic_load((uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <int WT, int BMAX, int CPT, int TPR, int R>
 struct Shape {
@@ -321,9 +333,10 @@ struct GateKernel {
   }
 
   // rec(slot, row, activations, bits) is called by wave 0 for every selected row, slot
-  // being its position in the tile's slice; returns the tile's selected-row count.
+  // being its position in the tile's slice; returns the tile's selected-row count and
+  // where its slice of the lists starts.
   template <class Rec>
-  __device__ static int run(const DecodeArgs& args, Rec&& rec) {
+  __device__ static int2 run(const DecodeArgs& args, Rec&& rec) {
     const DevArgs a = dev_args(args);
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -459,7 +472,7 @@ struct GateKernel {
       else if (tid - 1 < BMAX) v = sm.cnt[tid - 1];
       a.tile_cnt[w * kCnt + tid] = v;
     }
-    return sm.qlen;
+    return make_int2(sm.qlen, r0);
   }
 };
 
@@ -700,13 +713,24 @@ struct UpDownKernel {
 #pragma unroll
         for (int b = 0; b < BMAX; ++b) sm.qa[j][b] = b < nb ? a.sel_a[(size_t)b * a.f + o] : 0.f;
       }
-      stream(a, sm, nq, w);
+      NoBalance nobal;
+      stream(a, sm, nq, w, nobal);
     }
   }
 
-  // Up and down rows of share entries [0, nq) (rows, activations and bits in sm), then
-  // the workgroup's partial of y in partial rows w RPG .. w RPG + RPG - 1.
-  __device__ static void stream(const DevArgs& a, Smem& sm, int nq, int w) {
+  // Up and down rows of list entries (rows, activations and bits in sm), then the
+  // workgroup's partial of y in partial rows w RPG .. w RPG + RPG - 1. Without a balancer
+  // the entries are [0, nq). With one, the first three steps take entries
+  // [0, min(nq, 3 RG)); after the second step is processed the balancer settles the list
+  // (the tail of a long one given away, others' entries appended to a short one) and
+  // the steps continue from there.
+  struct NoBalance {
+    __device__ bool active() const { return false; }
+    __device__ void load_counts(const DevArgs&) {}
+    __device__ int decide(const DevArgs&, Smem&, int covered) { return covered; }
+  };
+  template <class Bal>
+  __device__ static void stream(const DevArgs& a, Smem& sm, int nq, int w, Bal& bal) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rl = tid / TPR, cl = tid % TPR;
     const int nb = a.nb;
@@ -760,27 +784,39 @@ struct UpDownKernel {
         }
       };
 
-      const int nstep = (nq + RG - 1) / RG;
+      // lim: entries the steps may take; steps 0 to 2 cover [0, covered), later steps run
+      // on from there
+      constexpr int kPre = 3;  // steps issued before the balancer decides
+      const bool balanced = bal.active();
+      int lim = balanced ? min(nq, kPre * RG) : nq;
+      const int covered = min(lim, kPre * RG);
+      int nstep = balanced ? kPre : (nq + RG - 1) / RG;
       uint4 a0[R][CPT], a1[R][CPT], b0[R][CPT], b1[R][CPT];
       auto step = [&](int s) -> StepDesc {
         StepDesc sd{STEP_NONE, 0, 0};
-        if (s < nstep) {
+        const int base = s < kPre ? s * RG : covered + (s - kPre) * RG;
+        if (s < nstep && base < lim) {
           sd.kind = STEP_UPDOWN;
-          sd.base = s * RG;
-          sd.n = min(RG, nq - sd.base);
+          sd.base = base;
+          sd.n = min(RG, lim - base);
         }
         return sd;
       };
       StepDesc sa = step(0);
-      issue(a, sm, sa, nq, rl, cl, a0, a1);
+      issue(a, sm, sa, lim, rl, cl, a0, a1);
       for (int s = 0; s < nstep; s += 2) {
         const StepDesc sb = step(s + 1);
-        issue(a, sm, sb, nq, rl, cl, b0, b1);
+        issue(a, sm, sb, lim, rl, cl, b0, b1);
         process(sa, a0, a1);
+        if (balanced && s == 0) bal.load_counts(a);
         if (s + 1 >= nstep) break;
         sa = step(s + 2);
-        issue(a, sm, sa, nq, rl, cl, a0, a1);
+        issue(a, sm, sa, lim, rl, cl, a0, a1);
         process(sb, b0, b1);
+        if (balanced && s == 0) {
+          lim = bal.decide(a, sm, covered);
+          nstep = kPre + (max(lim - covered, 0) + RG - 1) / RG;
+        }
       }
 
       // ---- partial of y (read by the reduce kernel after this launch completes)
@@ -1017,6 +1053,9 @@ struct ReduceKernel {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ri = blockIdx.x;
     const int nb = a.nb;
+    // the balancer's count words go back to zero for the next call
+    if (a.flags)
+      for (int i = ri * kRT + tid; i < a.G; i += gridDim.x * kRT) a.flags[i] = 0u;
     if (a.y && ri < a.n_red) {
       const int L = nb * a.d;
       const int nck = (L + kRedCols - 1) / kRedCols;
@@ -1075,6 +1114,131 @@ __global__ __launch_bounds__(kNT) void decode_gate_kernel(DecodeArgs a) {
   GateKernel<WT, BMAX, CPT, TPR, R>::run(a, [](int, int, const auto&, uint32_t) {});
 }
 
+// Balancer of the one-token up/down (flags non-null, G <= kBalMaxTiles, every tile
+// resident at once). A tile's share of up/down rows follows its active count, so the
+// slowest tile used to finish about 6 us after the median one. Each tile now publishes
+// its count (its entries first, through to memory); during its first two up/down steps
+// every workgroup reads all counts and derives the same assignment from them: with
+// T = ceil(N / G) for N active rows over G tiles, tile t keeps
+// k_t = max(min(c_t, T), min(c_t, 3 RG)) of its c_t entries (its first three steps are
+// already under way) and gives the rest away; the given-away entries, in tile order,
+// fill the shortfalls T - k_t of the other tiles, in tile order. The assignment depends
+// on the counts only, so every workgroup sums the same rows in the same order on every
+// run and y stays deterministic. The counts live in the workspace header, which the
+// reduce kernel clears again.
+// It costs a write-through of the tile's list and a wait for it, the count round trip,
+// and for a workgroup that takes rows, a round trip for their entries. That pays only
+// where tiles carry much up/down work: rows wider than 8 KB. One token, graph replay:
+// d 8192, f 28672: 148.3 against 154.0 us per call at 50% sparsity, 109.2 against 112.6
+// at 80%, 98.5 against 98.0 at 90%; d 5120, f 13824: 56.5 against 58.1 at 50%. With 8 KB
+// rows it lost: 37.6 against 37.2 us at d 4096, f 11008, 50%; 29.6 against 26.7 at 90%;
+// 52.2 against 51.5 at d 3584, f 18944.
+constexpr int kBalMaxTiles = 256;
+constexpr uint32_t kPublished = 0x80000000u;
+
+struct BalSmem {
+  int cnt[kBalMaxTiles];
+  int epre[kBalMaxTiles + 1];  // entries given away by the tiles before t
+  int dpre[kBalMaxTiles + 1];  // shortfalls of the tiles before t
+  int wsum[3][kNW];
+};
+
+template <int RG>
+struct Balancer {
+  BalSmem& bs;
+  bool on;
+  int G, w, nown, n_total;
+  uint32_t cw;  // count word of tile threadIdx.x, loaded when the up/down starts
+
+  __device__ bool active() const { return on; }
+
+  static constexpr int kPre = 3;  // up/down steps issued before the decision
+  __device__ static int keep_of(int c, int T) { return max(min(c, T), min(c, kPre * RG)); }
+
+  // the count words, loaded after the first up/down step (most tiles have published by
+  // the time they are used, one step later)
+  __device__ void load_counts(const DevArgs& a) {
+    if ((int)threadIdx.x < G) cw = ld_through(a.flags + threadIdx.x);
+  }
+
+  // Every tile's count (waiting for tiles still gating), the assignment, and this
+  // workgroup's list: its first keep entries, then its share of the given-away ones
+  // appended. Returns the list length.
+  template <class SmemT>
+  __device__ int decide(const DevArgs& a, SmemT& sm, int covered) {
+    (void)covered;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t v = cw;
+    if (tid < G) {
+      uint32_t spins = 0;
+      while (!(v & kPublished)) {
+        if (++spins > (1u << 20)) break;  // never expected: all G tiles run at once
+        __builtin_amdgcn_s_sleep(2);
+        v = ld_through(a.flags + tid);
+      }
+    }
+    // a tile has at most kTMax rows; the clamp keeps every index below in bounds even if
+    // the header held something other than zeros when the call started
+    const int c = tid < G ? min((int)(v & ~kPublished), kTMax) : 0;
+    auto incl = [&](int x) {  // inclusive scan over the wave
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const int u = __shfl_up(x, m, 64);
+        if (lane >= m) x += u;
+      }
+      return x;
+    };
+    const int ic = incl(c);
+    if (lane == 63) bs.wsum[0][wave] = ic;
+    if (tid < G) bs.cnt[tid] = c;
+    __syncthreads();
+    int N = 0;
+#pragma unroll
+    for (int i = 0; i < kNW; ++i) N += bs.wsum[0][i];
+    const int T = (N + G - 1) / G;
+    const int kt = keep_of(c, T);
+    const int ex = c - kt;                             // given away by tile tid
+    const int df = tid < G ? max(T - kt, 0) : 0;       // taken by tile tid
+    const int ie = incl(ex), id = incl(df);
+    if (lane == 63) {
+      bs.wsum[1][wave] = ie;
+      bs.wsum[2][wave] = id;
+    }
+    __syncthreads();
+    int be = 0, bd = 0;
+#pragma unroll
+    for (int i = 0; i < kNW; ++i) {
+      be += i < wave ? bs.wsum[1][i] : 0;
+      bd += i < wave ? bs.wsum[2][i] : 0;
+    }
+    if (tid <= G) {  // G < kNT: thread G writes the totals
+      bs.epre[tid] = be + ie - ex;
+      bs.dpre[tid] = bd + id - df;
+    }
+    __syncthreads();
+    const int keep = keep_of(nown, T);
+    const int etot = bs.epre[G];
+    const int e0 = min(bs.dpre[w], etot), e1 = min(bs.dpre[w] + max(T - keep, 0), etot);
+    const int ns = max(e1 - e0, 0);
+    for (int i = tid; i < ns; i += kNT) {
+      const int k = e0 + i;
+      int lo = 0, hi = G;  // the tile whose given-away range holds k: epre[lo] <= k < epre[lo + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (bs.epre[mid] <= k) lo = mid;
+        else hi = mid;
+      }
+      const int slot = min(share_begin(lo, n_total, G) + keep_of(bs.cnt[lo], T) + (k - bs.epre[lo]), a.f - 1);
+      const uint32_t row = ld_through(reinterpret_cast<const SFN_GLOBAL uint32_t*>(a.sel_idx + slot));
+      sm.qrow[keep + i] = (int)min(row, (uint32_t)(a.f - 1));
+      sm.qa[keep + i][0] = __uint_as_float(ld_through(reinterpret_cast<const SFN_GLOBAL uint32_t*>(a.sel_a + slot)));
+      sm.qbits[keep + i] = 1;
+    }
+    __syncthreads();
+    return keep + ns;
+  }
+};
+
 // Gate and up/down of one tile in one workgroup: the tile's selected rows are recorded
 // in LDS as the gate finds them, and the same workgroup then streams their up and down
 // rows and writes its partial of y. No list crosses workgroups, so the up/down launch
@@ -1086,15 +1250,33 @@ __global__ __launch_bounds__(kNT) void decode_gate_kernel(DecodeArgs a) {
 template <int WT, int BMAX, int CPT, int TPR, int RGATE, int RUP>
 __global__ __launch_bounds__(kNT) void decode_gate_local_kernel(DecodeArgs args) {
   using UD = UpDownKernel<WT, BMAX, CPT, TPR, RUP>;
+  static_assert(BMAX == 1, "one token");
   __shared__ typename UD::Smem usm;
-  const int n = GateKernel<WT, BMAX, CPT, TPR, RGATE>::run(
+  __shared__ BalSmem bsm;
+  const int2 go = GateKernel<WT, BMAX, CPT, TPR, RGATE>::run(
       args, [&](int slot, int row, const auto& av, uint32_t bits) {
         usm.qrow[slot] = row;
         usm.qbits[slot] = (uint8_t)bits;
 #pragma unroll
         for (int b = 0; b < BMAX; ++b) usm.qa[slot][b] = av[b];
       });
-  UD::stream(dev_args(args), usm, n, blockIdx.x);
+  const DevArgs a = dev_args(args);
+  const int tid = threadIdx.x, w = blockIdx.x;
+  const int n_total = a.cand ? min(max(*a.n_cand, 0), a.f) : a.f;
+  Balancer<UD::RG> bal{bsm, a.flags != nullptr, a.G, w, go.x, n_total, kPublished};
+  if (bal.on) {
+    // the tile's entries, then its count, through to memory for the other workgroups
+    for (int j = tid; j < go.x; j += kNT) {
+      st_through(reinterpret_cast<SFN_GLOBAL uint32_t*>(a.sel_idx + go.y + j), (uint32_t)usm.qrow[j]);
+      st_through(reinterpret_cast<SFN_GLOBAL uint32_t*>(a.sel_a + go.y + j), __float_as_uint(usm.qa[j][0]));
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have reached memory
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (tid == 0) st_through(a.flags + w, kPublished | (uint32_t)go.x);
+  }
+  UD::stream(a, usm, go.x, w, bal);
 }
 
 template <int WT, int BMAX, int CPT, int TPR, int R>
@@ -1103,6 +1285,19 @@ __global__ __launch_bounds__(kNT) void decode_updown_kernel(DecodeArgs a) {
 }
 
 __global__ __launch_bounds__(512) void decode_reduce_kernel(DecodeArgs a, int P) { ReduceKernel::run(a, P); }
+
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = -1;
+    cache[dev] = n;
+  }
+  return cache[dev] > 0 ? cache[dev] : 0;
+}
 
 // Workgroups of the reduce kernel: the column chunks of y (n_red), and when the index
 // lists are asked for, at least one workgroup per four gate tiles (G is the gate's tile
@@ -1125,8 +1320,11 @@ hipError_t launch_pair(const DecodeArgs& a, hipStream_t s) {
   DecodeArgs g = a;  // gate tiles G, up/down workgroups Gu
   g.Gu = a.G;
   const bool mfma = WT == WT_BF16 && !a.cand && !a.pl && a.nb >= kMfmaGateMinBatch && mfma_gate_tiles(a.f) <= kGMax;
-  // one token: each tile streams the up/down rows of its own selected rows
+  // one token: each tile streams the up/down rows of its own selected rows, balanced
+  // through the header words for rows wider than 8 KB when every tile can be resident
+  // at once
   const bool local = BMAX == 1 && a.y;
+  g.flags = local && CPT >= 2 && a.G <= kBalMaxTiles && a.G <= device_cus() ? a.flags : nullptr;
   if (mfma) {
     g.G = mfma_gate_tiles(a.f);
     hipLaunchKernelGGL((decode_gate_mfma_kernel<BMAX>), dim3(g.G), dim3(256), 0, s, g);
@@ -1150,7 +1348,9 @@ __global__ __launch_bounds__(kNT) void decode_parallel_kernel(DecodeArgs a) {
 }
 
 template <int WT, int CPT, int TPR, int R>
-hipError_t launch_parallel(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_parallel(const DecodeArgs& a0, hipStream_t s) {
+  DecodeArgs a = a0;
+  a.flags = nullptr;
   hipLaunchKernelGGL((decode_parallel_kernel<WT, CPT, TPR, R>), dim3(a.G), dim3(kNT), 0, s, a);
   hipLaunchKernelGGL(decode_reduce_kernel, dim3(reduce_grid(a)), dim3(ReduceKernel::kRT), 0, s, a,
                      a.G * (kNT / TPR));
@@ -1252,6 +1452,7 @@ void decode_carve(DecodeArgs& a, void* ws, int wb) {
   a.sel_bits = reinterpret_cast<uint8_t*>(p + off);
   off = align256(off + (size_t)a.f);
   a.part = reinterpret_cast<float*>(p + off);
+  a.flags = reinterpret_cast<uint32_t*>(p);  // the header (the launcher decides whether to use it)
 }
 
 hipError_t launch_decode_parallel(const DecodeArgs& a, int wdtype, hipStream_t s) {

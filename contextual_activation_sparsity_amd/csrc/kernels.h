@@ -10,9 +10,10 @@
 namespace sfn {
 
 // Workspace layout shared by every call on a workspace:
-//   [0, kWsHeader)      reserved for words that persist between calls (none are used:
-//                       every cross-workgroup hand-off is a kernel boundary or lives in
-//                       per-call scratch); zero-filled once by the caller
+//   [0, kWsHeader)      words that must be zero when a call starts: zero-filled once by
+//                       the caller, and every call that sets some clears them again in
+//                       its last launch (the one-token decode publishes its tiles' active
+//                       counts there for the balancer)
 //   [kWsHeader, ...)    per-call scratch, rewritten by each call before it is read
 // Scratch of one call may overlap scratch of another.
 constexpr size_t kWsHeader = 2048;
@@ -36,6 +37,9 @@ struct DecodeArgs {
   float* sel_a;       // [4, f]: their activations
   uint8_t* sel_bits;  // [f]: their per-token mask bits
   float* part;        // [G * rows side by side, nb, d]
+  // One word per gate tile in the workspace header (zero between calls), or null: the
+  // one-token decode balances its up/down work through them (the launcher decides).
+  uint32_t* flags;
   // Predict mode (pl non-null; one token): each tile's candidates are {i : L_i z + pb_i >
   // ptau_i} over its own rows instead of a share of a candidate list; z = Q x from the
   // predictor's first launch, r = rank.

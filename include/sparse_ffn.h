@@ -36,8 +36,10 @@
  *     the caller's next synchronisation. No C++ exception crosses the ABI.
  *   - Workspace: `ws` of `ws_bytes` bytes (256-byte aligned), sized by the
  *     *_workspace_size queries. Its first 2 KiB are reserved and must be zero-filled
- *     once when the workspace is allocated (e.g. torch.zeros); no call changes them.
- *     Everything after them is scratch each call rewrites before reading, so any
+ *     once when the workspace is allocated (e.g. torch.zeros). A call may use them
+ *     between its own kernels (the one-token decode publishes per-tile counts there)
+ *     but its last kernel zeroes them again, so they are zero whenever no call is in
+ *     flight. Everything after them is scratch each call rewrites before reading, so any
  *     sequence of calls on one stream may share one workspace (sized for the largest
  *     of them). Calls that may run concurrently (different streams) need distinct
  *     workspaces.

@@ -28,7 +28,7 @@ def _tol(dtype):
 
 
 def _header_clear(ws):
-    """The first 2 KiB of a workspace are reserved: no call may change them."""
+    """The first 2 KiB of a workspace are reserved: zero whenever no call is in flight."""
     return not bool(ws[:2048].any().item())
 
 
@@ -125,6 +125,34 @@ def test_llama3_70b_layer():
     """Full Llama-3-70B FFN shape (d 8192: two 16-byte chunks per thread and row)."""
     w = inputs.workload(4)
     _case(w, w.d, w.f, 0.5, 2)
+
+
+@pytest.mark.parametrize("d,f,k", [(8192, 6000, 0.5), (5120, 7000, 0.8)])
+def test_balanced_tiles_determinism_and_shared_workspace(d, f, k):
+    """One token with rows wider than 8 KB: the tiles balance their up/down rows through
+    count words in the workspace header. Against the oracle (in _case); then y and the
+    index lists bitwise equal over repeated calls, also when calls of other kinds (a batch
+    of four, calibration, the dense chunk) use the same workspace in between, and the
+    header zero after every call."""
+    w = inputs.workload(4)
+    layer, _, dev, host, t = _case(w, d, f, k, 2)
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, 16))
+    xs_raw = inputs.tokens(w, 5, inputs.STREAM_DECODE, d=d)
+    x1, x4 = to_dev(xs_raw[:1], w.dtype), to_dev(xs_raw[1:5], w.dtype)
+    xc = to_dev(inputs.tokens(w, 16, inputs.STREAM_CAL, d=d), w.dtype)
+    t_out = torch.zeros(1, dtype=torch.float32, device="cuda")
+    y16 = torch.empty((16, d), dtype=torch.float32, device="cuda")
+    y0, i0, n0 = run_decode(layer, x1, t, ws)
+    for rep in range(3):
+        say(f"    repeat {rep}")
+        run_decode(layer, x4, t, ws)
+        B.sparse_ffn_calibrate(layer, xc, k, t_out, ws)
+        B.ffn_dense_chunk(layer, xc, y16, ws)
+        torch.cuda.synchronize()
+        assert _header_clear(ws)
+        y1, i1, n1 = run_decode(layer, x1, t, ws)
+        assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+        assert n0[0] == n1[0] and np.array_equal(i0[0][:n0[0]], i1[0][:n1[0]])
 
 
 def test_qwen2_7b_layer():
