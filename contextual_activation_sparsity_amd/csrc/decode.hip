@@ -321,8 +321,10 @@ struct GateKernel {
         w1[k][c] = ldg16(p + (size_t)g1 * rb + (size_t)ch * 16);
       }
     }
+    // an empty share (no candidates) has no rowid entries: fetch row 0's bytes instead of
+    // indexing with whatever the LDS holds
     const int lb = min(sd.base + (lane % RS), lrmax);
-    const int gb = cand_mode ? sm.rowid[lb] : r0 + lb;
+    const int gb = nrows == 0 ? 0 : cand_mode ? sm.rowid[lb] : r0 + lb;
     bias = a.bias ? a.bias[gb] : gp(g_zero_f32)[0];
     // raw bytes: tested only when the step is processed, so no wait is forced here
 #pragma unroll

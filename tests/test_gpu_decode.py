@@ -278,6 +278,28 @@ def test_candidate_mode_reglu():
             assert np.all(y[0] == 0.0)
 
 
+@pytest.mark.parametrize("d,want_y", [(1024, True), (1024, False), (8192, True)])
+def test_empty_candidate_list(d, want_y):
+    """n_cand = 0 leaves every gate tile without rows (regression: a tile with no rows
+    once fetched its bias through a row index read from LDS it had never written). The
+    call must produce y = 0 and no active rows, with a bias present to be fetched: the
+    one-token loop (d 1024), the gate alone (no y) and the balanced path (d 8192)."""
+    w = inputs.workload(3)
+    f = 3000
+    raw = inputs.reglu_layer(w, 0, d=d, f=f)
+    layer = B.FFNLayer(to_dev(raw["w_gate"], "bf16"), to_dev(raw["w_up"], "bf16"), to_dev(raw["w_down_t"], "bf16"),
+                       b_gate=torch.from_numpy(raw["b_gate"]).cuda(), act=B.SFN_ACT_RELU)
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, 1))
+    xd = to_dev(inputs.tokens(w, 1, inputs.STREAM_DECODE, d=d), "bf16")
+    cand = torch.zeros(f, dtype=torch.int32, device="cuda")
+    n_cand = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        y, idx, n_act = run_decode(layer, xd, 0.0, ws, want_y=want_y, cand=cand, n_cand=n_cand)
+        assert np.all(n_act == 0)
+        if want_y:
+            assert np.all(y == 0.0)
+
+
 def test_one_workspace_shared_by_every_call():
     """calibrate -> decode -> dense chunk -> predictor -> decode -> calibrate -> decode on a
     single workspace: each call must leave the reserved header as it found it
