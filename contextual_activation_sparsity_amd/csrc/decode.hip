@@ -728,6 +728,7 @@ struct UpDownKernel {
   // the steps continue from there.
   struct NoBalance {
     __device__ bool active() const { return false; }
+    __device__ bool poisoned() const { return false; }
     __device__ void load_counts(const DevArgs&) {}
     __device__ int decide(const DevArgs&, Smem&, int covered) { return covered; }
   };
@@ -822,6 +823,14 @@ struct UpDownKernel {
       }
 
       // ---- partial of y (read by the reduce kernel after this launch completes)
+      if (bal.poisoned()) {
+#pragma unroll
+        for (int b = 0; b < BMAX; ++b)
+#pragma unroll
+          for (int c = 0; c < CPT; ++c)
+#pragma unroll
+            for (int v = 0; v < KV; ++v) acc[b][c][v] = __builtin_nanf("");
+      }
       SFN_GLOBAL float* prow = a.part + ((size_t)(w * RPG + rl) * nb) * a.d;
 #pragma unroll
       for (int b = 0; b < BMAX; ++b) {
@@ -1150,9 +1159,11 @@ struct Balancer {
   BalSmem& bs;
   bool on;
   int G, w, nown, n_total;
-  uint32_t cw;  // count word of tile threadIdx.x, loaded when the up/down starts
+  uint32_t cw;           // count word of tile threadIdx.x, loaded when the up/down starts
+  bool gave_up = false;  // a count never arrived: this workgroup's partial becomes NaN
 
   __device__ bool active() const { return on; }
+  __device__ bool poisoned() const { return gave_up; }
 
   static constexpr int kPre = 3;  // up/down steps issued before the decision
   __device__ static int keep_of(int c, int T) { return max(min(c, T), min(c, kPre * RG)); }
@@ -1170,15 +1181,23 @@ struct Balancer {
   __device__ int decide(const DevArgs& a, SmemT& sm, int covered) {
     (void)covered;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Every tile is resident at once (G <= CU count), so the wait ends once all have been
+    // dispatched; kernels of other streams can only delay that. The bound (seconds) is a
+    // guard: a workgroup that reaches it poisons its partial, so y is NaN, not wrong.
     uint32_t v = cw;
+    bool late = false;
     if (tid < G) {
       uint32_t spins = 0;
       while (!(v & kPublished)) {
-        if (++spins > (1u << 20)) break;  // never expected: all G tiles run at once
+        if (++spins > (1u << 24)) {
+          late = true;
+          break;
+        }
         __builtin_amdgcn_s_sleep(2);
         v = ld_through(a.flags + tid);
       }
     }
+    gave_up = __syncthreads_or(late) != 0;
     // a tile has at most kTMax rows; the clamp keeps every index below in bounds even if
     // the header held something other than zeros when the call started
     const int c = tid < G ? min((int)(v & ~kPublished), kTMax) : 0;

@@ -149,6 +149,11 @@ int sparse_ffn_calibrate(const sfn_ffn* ffn, const void* x_cal, int32_t n, float
  *   Fast LLM Inference", Figure 3). Requires B == 1 and mask_in == NULL.
  * active_idx [B, f] int32 / n_active [B] int32 (device) or NULL: token b's active
  *   neurons in ascending order and their count.
+ * One token with rows wider than 8 KB (d > 4096 in bf16): the workgroups of the call
+ *   share out their up/down rows, so each waits until all of them have run their gate
+ *   part. On a device with at least as many compute units as workgroups they are all
+ *   resident at once; kernels on other streams can only delay them. Should the wait
+ *   exceed several seconds, y comes out NaN rather than wrong.
  */
 int sparse_ffn_decode(const sfn_ffn* ffn, const void* x, int32_t B, const float* t,
                       const int32_t* cand, const int32_t* n_cand, const uint8_t* mask_in,
