@@ -116,8 +116,13 @@ __device__ __forceinline__ DevArgs dev_args(const DecodeArgs& h) {
 __device__ __attribute__((aligned(16))) float g_zero_f32[4];
 __device__ __attribute__((aligned(16))) uint8_t g_zero_u8[16];
 
-// First entry of share w when n entries are split over G workgroups.
-__device__ __forceinline__ int share_begin(int w, int n, int G) { return (int)((long long)w * n / G); }
+// First entry of share w when n entries are split over G workgroups. Here w <= 1024
+// workgroups and n <= 2^18 rows (SFN_MAX_F), so w n < 2^28 and 32-bit unsigned
+// arithmetic is exact; a 64-bit division would cost over a hundred instructions in every
+// workgroup's prologue, ahead of its first weight load.
+__device__ __forceinline__ int share_begin(int w, int n, int G) {
+  return (int)((uint32_t)w * (uint32_t)n / (uint32_t)G);
+}
 
 // Words other workgroups read during the same launch: relaxed device-scope atomics,
 // which go through to memory past this XCD's L2 (the L2s of the eight XCDs are not
