@@ -155,6 +155,32 @@ def test_balanced_tiles_determinism_and_shared_workspace(d, f, k):
         assert n0[0] == n1[0] and np.array_equal(i0[0][:n0[0]], i1[0][:n1[0]])
 
 
+def test_balanced_tiles_uneven_counts():
+    """The balancer's hand-offs under very uneven tiles (rows wider than 8 KB, mask
+    override): every active row in the first tiles, one active row, every row active,
+    and a comb that leaves alternate tiles empty. y against the oracle on the same mask,
+    bitwise equal on a second call, header zero after each call."""
+    w = inputs.workload(4)
+    d, f = 8192, 4000
+    raw, dev, host = swiglu_layer_dev(w, 0, d=d, f=f)
+    Wg, Wu, Dt = host["w_gate"], host["w_up"], host["w_down_t"]
+    layer = B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"])
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, 1))
+    x_raw = inputs.tokens(w, 1, inputs.STREAM_DECODE, d=d)
+    x = to_f64(x_raw, w.dtype)[0]
+    xd = to_dev(x_raw, w.dtype)
+    rows_per_tile = f / 256
+    masks = {"first tiles": np.arange(f) < 300, "one row": np.arange(f) == 2345, "all": np.ones(f, bool),
+             "alternate tiles": (np.floor(np.arange(f) / rows_per_tile).astype(int) % 2) == 0}
+    for name, m in masks.items():
+        say(f"    {name}: {int(m.sum())} active")
+        y, idx, n_act = run_decode(layer, xd, None, ws, mask=m[None].astype(np.uint8))
+        assert n_act[0] == m.sum() and np.array_equal(idx[0][:n_act[0]], np.flatnonzero(m))
+        assert normwise_err(y[0], oracle.masked_ffn(Wg, Wu, Dt, x, m, "silu")) <= TOL_BF16
+        y2, _, _ = run_decode(layer, xd, None, ws, mask=m[None].astype(np.uint8))
+        assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
 def test_qwen2_7b_layer():
     """SparseQwen2-7B FFN shape: d 3584 is 448 16-byte chunks, not a power of two, so
     part of each row's threads hold no chunk."""
