@@ -1,4 +1,4 @@
-// Dense FFN over a chunk of up to 16 tokens on matrix cores: the Sirius verification
+// Dense FFN over a chunk of 2 to 16 tokens on matrix cores: the Sirius verification
 // pass ("SIRIUS: Contexual Sparisty with Correction for Efficient LLMs", Approach: the
 // full model re-runs a chunk of sparse-generated tokens in parallel with the weights the
 // sparse model shares).
@@ -251,11 +251,19 @@ int chunk_splits(int d, int f) {
 
 }  // namespace
 
+// Chunks of at most this many bf16 tokens run through the decode kernels with threshold 0
+// (every neuron that contributes). One token, graph replay: 48.8 against 58.9 us at d
+// 4096, f 11008; 61.0 against 76.4 at f 14336; 218.9 against 249.0 at d 8192, f 28672.
+// With two to four tokens neither path wins everywhere (60-79 us against 60-79 at d
+// 4096; 230-242 against 249-251 at d 8192), so they stay on the matrix cores.
+constexpr int kDecodeDenseMax = 1;
+
 size_t chunk_workspace_bytes(int d, int f, int wdtype, int n) {
   if (wdtype != SFN_BF16) {
     // fp32 weights run through the decode kernel, 4 tokens at a time
     return decode_workspace_bytes(d, f, 4, n > 1 ? 4 : 1);
   }
+  if (n <= kDecodeDenseMax) return decode_workspace_bytes(d, f, 2, n);
   const int S = chunk_splits(d, f);
   size_t bytes = kWsHeader;
   bytes += (size_t)SFN_MAX_CHUNK * ((f + 7) & ~7) * sizeof(uint16_t);
@@ -266,8 +274,9 @@ size_t chunk_workspace_bytes(int d, int f, int wdtype, int n) {
 }
 
 hipError_t launch_dense_chunk(const sfn_ffn& ffn, const void* x, int n, float* y, void* ws, hipStream_t stream) {
-  if (ffn.wdtype != SFN_BF16) {
+  if (ffn.wdtype != SFN_BF16 || n <= kDecodeDenseMax) {
     // |act(g)| > 0 keeps every neuron that contributes, so this is the dense FFN.
+    const int wb = ffn.wdtype == SFN_BF16 ? 2 : 4;
     DecodeArgs a{};
     a.wg = static_cast<const char*>(ffn.w_gate);
     a.wu = static_cast<const char*>(ffn.w_up);
@@ -275,18 +284,18 @@ hipError_t launch_dense_chunk(const sfn_ffn& ffn, const void* x, int n, float* y
     a.bias = ffn.b_gate;
     a.d = ffn.d;
     a.f = ffn.f;
-    a.nch = ffn.d * 4 / 16;
-    a.row_bytes = ffn.d * 4;
+    a.nch = ffn.d * wb / 16;
+    a.row_bytes = ffn.d * wb;
     a.act = ffn.act;
     a.G = decode_grid(ffn.f);
-    decode_carve(a, ws, 4);
+    decode_carve(a, ws, wb);
     for (int j0 = 0; j0 < n; j0 += SFN_MAX_BATCH) {
       const int nb = n - j0 < SFN_MAX_BATCH ? n - j0 : SFN_MAX_BATCH;
       a.x = static_cast<const char*>(x) + (size_t)j0 * a.row_bytes;
       a.y = y + (size_t)j0 * ffn.d;
       a.nb = nb;
       a.n_red = decode_reducers(a.G, nb, ffn.d);
-      hipError_t e = launch_decode(a, SFN_F32, stream);
+      hipError_t e = launch_decode(a, ffn.wdtype, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;

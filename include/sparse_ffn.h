@@ -221,8 +221,10 @@ int sparse_ffn_decode_svd(const sfn_ffn* ffn, const sfn_svd* svd, const void* x,
  * ("SIRIUS: Contexual Sparisty with Correction for Efficient LLMs", Approach: the full
  * model checks a chunk of sparse-generated tokens in parallel with the shared weights):
  *   Y[j, :] = sum_i act(g_ji) u_ji Dt[i, :]   for every neuron, fp32 [n, d].
- * bf16 weights run on matrix cores (bf16 products, fp32 accumulation; the intermediate
- * h = act(g) u is rounded to bf16 for the second product).
+ * bf16 weights with n >= 2 run on matrix cores (bf16 products, fp32 accumulation; the
+ * intermediate h = act(g) u is rounded to bf16 for the second product). One token, and
+ * fp32 weights, run through the decode kernels with threshold 0 (every neuron with
+ * act(g) != 0, i.e. every one that contributes), with h in fp32.
  *   x  [n, d] in ffn->wdtype;  y [n, d] fp32
  */
 int ffn_dense_chunk(const sfn_ffn* ffn, const void* x, int32_t n, float* y, void* ws,
