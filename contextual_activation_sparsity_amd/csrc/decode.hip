@@ -27,6 +27,8 @@
 //    tile streams the up/down rows of that tile's active rows right after, from a copy of
 //    the list in LDS. A tile's share follows the spread of its active count, but the
 //    separate launch, its scan over the tile counts and its gather of a share cost more.
+//    For rows wider than 8 KB the tiles also even out their shares among themselves
+//    through count words in the workspace header (Balancer).
 //  * Batches (decode_updown_kernel, launch 2 of 3): the active lists of all tiles form one
 //    concatenated list and each of Gu workgroups takes an equal share of it (a prefix over
 //    the tile counts in LDS): the union rows of several tokens are many, and an even split
