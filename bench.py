@@ -711,7 +711,7 @@ def main():
         ms_k, nact_k, bytes_k = measure(k, steps_tok, args.mode)
         st = ms_k / K
         result_sweep.append({"sparsity": k, "tokens_per_s": 1e3 / st, "ms_per_step": st,
-                             "measured_density": float(nact_k.mean() / f),
+                             "measured_density": float(nact_k.mean() / f), "bytes_per_token": bytes_k,
                              "step_gbs": bytes_k / (st * 1e-3) / 1e9})
         log(f"  sparsity {k}: {1e3 / st:.1f} tokens/s, density {nact_k.mean() / f:.4f}")
 
@@ -753,7 +753,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": stack.w.name, "layers": L, "d": d, "f": f, "batch": 1, "sparsity": args.sparsity,
                    "calibration_tokens": stack.w.n_cal, "measured_density": float(nact.mean() / f),
-                   "mode": args.mode, "step_gbs": bytes_tok / (ms_step * 1e-3) / 1e9},
+                   "mode": args.mode, "bytes_per_token": bytes_tok,
+                   "step_gbs": bytes_tok / (ms_step * 1e-3) / 1e9},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "dense_path": dense,
