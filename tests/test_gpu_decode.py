@@ -100,8 +100,10 @@ def test_ragged_shapes_bf16(d, f):
     _case(w, d, f, 0.5, 4)
 
 
-@pytest.mark.parametrize("d,f", [(96, 500), (1024, 1030), (2048, 3000)])
+@pytest.mark.parametrize("d,f", [(96, 500), (1024, 1030), (2048, 3000), (4096, 2500), (8192, 1500)])
 def test_ragged_shapes_f32(d, f):
+    """fp32 rows of up to 32 KB; from 16 KB (d 4096) on, one token takes the balanced
+    per-tile up/down."""
     w = inputs.workload(0)
     _case(w, d, f, 0.6, 4)
 
