@@ -273,10 +273,12 @@ def test_mask_only_and_empty_mask_and_determinism():
     assert n1[0] == 0 and np.all(y1 == 0.0)
 
 
-def test_candidate_mode_reglu():
-    """Gate evaluated on a candidate list only (ReLU, bias): oracle reglu_sequential."""
+@pytest.mark.parametrize("d", [2048, 8192])
+def test_candidate_mode_reglu(d):
+    """Gate evaluated on a candidate list only (ReLU, bias): oracle reglu_sequential. At
+    d 8192 the tiles (shares of the candidate list) balance their up/down rows."""
     w = inputs.workload(3)
-    d, f = 2048, 5000
+    f = 5000
     raw = inputs.reglu_layer(w, 0, d=d, f=f)
     Wg, Wu, Dt = (to_f64(raw[k], "bf16") for k in ("w_gate", "w_up", "w_down_t"))
     b = raw["b_gate"].astype(np.float64)
