@@ -89,3 +89,50 @@ def test_graph_replays_match_eager():
         for k, v in out.items():
             assert torch.equal(v, ref[k]), f"replay {rep}: {k} differs from the eager result"
         assert not bool(ws[:2048].any().item())
+
+
+def test_graph_replays_balanced_one_token():
+    """One-token calls with rows wider than 8 KB (the tiles balance their up/down rows
+    through count words in the workspace header, zeroed again by each call's last kernel)
+    captured back to back in one graph, several layers on one workspace: every replay
+    reproduces the eager outputs bit for bit and leaves the header zero."""
+    w = inputs.workload(4)
+    d, f, n_layers = 8192, 3000, 3
+    say(f"[graph balanced] d={d} f={f} layers={n_layers}")
+    layers = []
+    for l in range(n_layers):
+        raw, dev, host = swiglu_layer_dev(w, l, d=d, f=f)
+        layers.append(B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"]))
+    ws = B.workspace(B.sparse_ffn_workspace_size(layers[0], 1))
+    X = to_dev(inputs.tokens(w, n_layers, inputs.STREAM_DECODE, d=d), "bf16")
+    t = torch.full((1,), 0.02, dtype=torch.float32, device="cuda")
+    Y = torch.empty((n_layers, d), dtype=torch.float32, device="cuda")
+    I = torch.empty((n_layers, f), dtype=torch.int32, device="cuda")
+    N = torch.empty((n_layers,), dtype=torch.int32, device="cuda")
+
+    def calls():
+        for l in range(n_layers):
+            B.sparse_ffn_decode(layers[l], X[l:l + 1], t, ws, y=Y[l:l + 1], active_idx=I[l:l + 1],
+                                n_active=N[l:l + 1])
+
+    def poison():
+        Y.fill_(float("nan"))
+        I.fill_(-7)
+        N.fill_(-7)
+
+    poison()
+    calls()
+    torch.cuda.synchronize()
+    ref = (Y.clone(), I.clone(), N.clone())
+    assert bool((ref[2] > 0).all()) and bool((ref[2] < f).all())
+    g = torch.cuda.CUDAGraph()
+    poison()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        poison()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, ref[0]) and torch.equal(I, ref[1]) and torch.equal(N, ref[2]), rep
+        assert not bool(ws[:2048].any().item())
