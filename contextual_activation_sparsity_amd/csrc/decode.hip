@@ -41,8 +41,9 @@
 // Last launch, reduce kernel: y = the sum of the partials, column slice by column slice,
 // in a fixed order, so y is deterministic; its workgroups also assemble the per-token
 // active index lists, each the slices of a share of the gate tiles. The kernel boundary
-// orders the partial stores before the loads: no device-scope atomics, fences or waits
-// anywhere in the decode path.
+// orders the partial stores before the loads. The decode path uses no fences; only the
+// balancer (one token, rows wider than 8 KB) exchanges words between workgroups of one
+// launch, with relaxed device-scope atomics.
 //
 // The one-pass kernel (parallel pipeline of the SVD predictor) reads the gate, up and
 // down rows of each candidate together and ends in the same reduce kernel.
