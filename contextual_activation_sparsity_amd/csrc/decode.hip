@@ -48,6 +48,8 @@
 // The one-pass kernel (parallel pipeline of the SVD predictor) reads the gate, up and
 // down rows of each candidate together and ends in the same reduce kernel.
 
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -1317,17 +1319,21 @@ __global__ __launch_bounds__(kNT) void decode_updown_kernel(DecodeArgs a) {
 
 __global__ __launch_bounds__(512) void decode_reduce_kernel(DecodeArgs a, int P) { ReduceKernel::run(a, P); }
 
-// Compute units of the current device (cached per device; 0 if unknown).
+// Compute units of the current device (cached per device; 0 if unknown). Host threads
+// may call this concurrently: every thread that finds the entry empty stores the same
+// value.
 int device_cus() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = -1;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
+    v = n;
   }
-  return cache[dev] > 0 ? cache[dev] : 0;
+  return v > 0 ? v : 0;
 }
 
 // Workgroups of the reduce kernel: the column chunks of y (n_red), and when the index
