@@ -369,6 +369,8 @@ def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4):
     w2 = inputs.workload(2)
     decode_leg("llama3_8b_b4_k50", w2, w2.d, w2.f, 4, 0.5, n_layers)
     decode_leg("llama3_8b_b1_k50", w2, w2.d, w2.f, 1, 0.5, n_layers)
+    decode_leg("llama3_8b_b4_k60", w2, w2.d, w2.f, 4, 0.6, n_layers)
+    decode_leg("llama3_8b_b1_k60", w2, w2.d, w2.f, 1, 0.6, n_layers)
     # sparse decode at the Llama-3-70B shape (d 8192: two 16-byte chunks per thread)
     w4 = inputs.workload(4)
     decode_leg("llama3_70b_b1_k50", w4, w4.d, w4.f, 1, 0.5, 2)

@@ -190,9 +190,11 @@ def test_qwen2_7b_layer():
     _case(w, w.d, w.f, 0.5, 2)
 
 
-def test_batch4_union_llama3_8b_layer():
+@pytest.mark.parametrize("k,n_tok", [(0.5, 8), (0.6, 4)])
+def test_batch4_union_llama3_8b_layer(k, n_tok):
+    """The Llama-3-8B layer at both of its sparsities, in batches of four."""
     w = inputs.workload(2)
-    layer, ws, dev, host, t = _case(w, w.d, w.f, 0.5, 8, batch=4)
+    layer, ws, dev, host, t = _case(w, w.d, w.f, k, n_tok, batch=4)
     # each token of the batch equals its single-token run (same mask, same output up to
     # the fixed reduction order of the split-k partials)
     xs_raw = inputs.tokens(w, 4, inputs.STREAM_DECODE)
