@@ -97,6 +97,34 @@ __device__ __forceinline__ float dpp_mov(float v) {
 }
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// gfx950 lane swaps (v_permlane32_swap / v_permlane16_swap): VALU moves, with no trip
+// through the LDS crossbar that a shuffle takes. BIT 32: the upper 32 lanes of a trade
+// places with the lower 32 lanes of b. BIT 16: the odd rows of 16 lanes of a trade places
+// with the even rows of b. Afterwards a lane without BIT holds in a and b what it and its
+// partner lane (l | BIT) held in a; a lane with BIT holds what its partner (l & ~BIT) and
+// it held in b. The whole wave must be active.
+template <int BIT>
+__device__ __forceinline__ void lane_swap(float& a, float& b) {
+  static_assert(BIT == 32 || BIT == 16, "half-wave or row swaps");
+  if constexpr (BIT == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+
+// v plus the v of lane l ^ BIT (BIT 16 or 32); the sum is the same in both lanes.
+template <int BIT>
+__device__ __forceinline__ float swap_pair_sum(float v) {
+  float a = v, b = v;
+  lane_swap<BIT>(a, b);
+  return a + b;
+}
+
 // Sum over all 64 lanes; every lane receives the total. Fixed pairing order, so the
 // result is the same on every run.
 __device__ __forceinline__ float wave_sum(float v) {
@@ -104,8 +132,8 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_mov<SFN_DPP_XOR2>(v);
   v += dpp_mov<SFN_DPP_HALF_MIRROR>(v);
   v += dpp_mov<SFN_DPP_ROW_MIRROR>(v);
-  v += shfl_xor_f(v, 16);
-  v += shfl_xor_f(v, 32);
+  v = swap_pair_sum<16>(v);
+  v = swap_pair_sum<32>(v);
   return v;
 }
 
@@ -130,16 +158,23 @@ template <int BIT, int H>
 __device__ __forceinline__ void halve_step(float* s) {
 #pragma unroll
   for (int i = 0; i < H; ++i) {
-    const float lo = s[i], hi = s[i + H];
-    const float keep = sel_upper<BIT>(lo, hi);
-    const float send = sel_upper<BIT>(hi, lo);
-    s[i] = keep + shfl_xor_f(send, BIT);
+    if constexpr (BIT >= 16) {
+      // one swap puts both operands of each lane's sum in place
+      float lo = s[i], hi = s[i + H];
+      lane_swap<BIT>(lo, hi);
+      s[i] = lo + hi;
+    } else {
+      const float lo = s[i], hi = s[i + H];
+      const float keep = sel_upper<BIT>(lo, hi);
+      const float send = sel_upper<BIT>(hi, lo);
+      s[i] = keep + shfl_xor_f(send, BIT);
+    }
   }
 }
 
 template <int BIT>
 __device__ __forceinline__ float lane_pair_sum(float v) {
-  if constexpr (BIT >= 16) return v + shfl_xor_f(v, BIT);
+  if constexpr (BIT >= 16) return swap_pair_sum<BIT>(v);
   else if constexpr (BIT == 8) return v + dpp_mov<SFN_DPP_ROW_MIRROR>(v);
   else if constexpr (BIT == 4) return v + dpp_mov<SFN_DPP_HALF_MIRROR>(v);
   else if constexpr (BIT == 2) return v + dpp_mov<SFN_DPP_XOR2>(v);
