@@ -260,7 +260,7 @@ __device__ void predict_tile(const DevArgs& a, PredSmem& ps, int r0, int nt, int
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       float acc = dot_l_z(wv[u][1], zc[1], dot_l_z(wv[u][0], zc[0], 0.f));
-      for (int m = 1; m < tpr; m <<= 1) acc += __shfl_xor(acc, m, 64);
+      acc = lt == 3 ? group_sum<8>(acc) : lt == 4 ? group_sum<16>(acc) : lt == 5 ? group_sum<32>(acc) : group_sum<64>(acc);
       const int row = (p0 + u) * rp + rl;
       if (cl == 0 && row < nt) ps.p[row] = acc;
     }

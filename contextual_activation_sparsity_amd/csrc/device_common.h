@@ -125,17 +125,25 @@ __device__ __forceinline__ float swap_pair_sum(float v) {
   return a + b;
 }
 
-// Sum over all 64 lanes; every lane receives the total. Fixed pairing order, so the
-// result is the same on every run.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_mov<SFN_DPP_XOR1>(v);
-  v += dpp_mov<SFN_DPP_XOR2>(v);
-  v += dpp_mov<SFN_DPP_HALF_MIRROR>(v);
-  v += dpp_mov<SFN_DPP_ROW_MIRROR>(v);
-  v = swap_pair_sum<16>(v);
-  v = swap_pair_sum<32>(v);
+// Sum over each aligned group of N consecutive lanes (N a power of two, at most 64);
+// every lane of a group receives its total. Each step adds a partner lane that lies in
+// the other half of the current group (a mirror or a swap; which lane of that half does
+// not matter, since all of them hold the same partial sum by then). Fixed pairing order,
+// so the result is the same on every run. The whole wave must be active.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "power-of-two group of lanes");
+  if constexpr (N >= 2) v += dpp_mov<SFN_DPP_XOR1>(v);
+  if constexpr (N >= 4) v += dpp_mov<SFN_DPP_XOR2>(v);
+  if constexpr (N >= 8) v += dpp_mov<SFN_DPP_HALF_MIRROR>(v);
+  if constexpr (N >= 16) v += dpp_mov<SFN_DPP_ROW_MIRROR>(v);
+  if constexpr (N >= 32) v = swap_pair_sum<16>(v);
+  if constexpr (N >= 64) v = swap_pair_sum<32>(v);
   return v;
 }
+
+// Sum over all 64 lanes; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
 // Lane select for the halving steps: hi in the lanes whose index has bit BIT set, lo in
 // the others, for BIT in {32, 16, 8, 4}. A DPP identity move whose row mask (lane groups

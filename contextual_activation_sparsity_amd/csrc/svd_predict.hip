@@ -119,8 +119,7 @@ __global__ __launch_bounds__(512) void svd_p_kernel(const char* __restrict__ l, 
       }
     }
     // reduce over the TPR lanes of the row (TPR divides 64, lanes contiguous)
-#pragma unroll
-    for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    acc = group_sum<TPR>(acc);
     if (cl == 0) s_p[rl + RPI * it] = acc;
   }
   __syncthreads();
