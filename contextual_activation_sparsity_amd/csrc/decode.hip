@@ -1349,7 +1349,17 @@ int reduce_grid(const DecodeArgs& g) {
 // kGMax tiles of 16 rows, no candidate list): its cost per row does not grow with the batch.
 constexpr int kMfmaGateMinBatch = 2;
 
-int mfma_gate_tiles(int f) { return (f + kMRows - 1) / kMRows; }
+// Tiles of the matrix-core gate: at most 16 rows each (rows split evenly over the tiles),
+// rounded up to a multiple of 256 workgroups while that stays within kGMax, so that every
+// compute unit of a 256-CU device holds the same number of tiles (all of them are
+// resident at once). At f 14336, 1024 tiles of 14 rows took 2.1-2.3 us less per
+// four-token call than 896 tiles of 16 rows, and at f 11008 768 tiles about 1 us less
+// than 688. The matrix-core gate is taken iff ceil(f / 16) <= kGMax, as before.
+int mfma_gate_tiles(int f) {
+  const int g = (f + kMRows - 1) / kMRows;
+  const int r = (g + 255) / 256 * 256;
+  return r <= kGMax ? r : g;
+}
 
 // RGATE / RUP: rows each thread holds per half step of the gate / per up-down step.
 template <int WT, int BMAX, int CPT, int TPR, int RGATE, int RUP>
