@@ -219,9 +219,10 @@ def test_partial_batches(batch):
 @pytest.mark.parametrize("d,f,batch", [(1024, 777, 3), (520, 2000, 4), (8192, 2000, 2), (2048, 16, 4),
                                        (128, 17, 2), (4096, 16384, 4)])
 def test_ragged_batches(d, f, batch):
-    """Batches on the matrix-core gate: tiles of 15 or 16 rows, a K range that ends
-    inside a stage (d 520), several stages (d 8192), one or two tiles in all (f 16, 17),
-    and the largest f it takes (16384 rows, 1024 tiles)."""
+    """Batches on the matrix-core gate, whose tile count is rounded up to a multiple of
+    256: tiles of a few rows (f 777, 2000), mostly empty tiles (f 16, 17: one row or none
+    per tile), a K range that ends inside a stage (d 520), several stages (d 8192), and the
+    largest f it takes (16384 rows, 1024 tiles of 16)."""
     w = inputs.workload(1)
     _case(w, d, f, 0.5, 2 * batch, batch=batch)
 
