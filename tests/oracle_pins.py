@@ -101,6 +101,22 @@ def pin_cats_golden():
         assert np.allclose(Y[0], want, rtol=1e-14, atol=0), (case, Y)
 
 
+def pin_threshold_band():
+    """Hand-worked band memberships (tests/golden/threshold_band.json): the edge
+    |score - t| = rel |t| is inside, the half-width scales with |t| (not |score|), a
+    zero threshold is widened only by the absolute floor, and per-token thresholds and
+    per-neuron floors broadcast over a [tokens, neurons] score array."""
+    fx = _load("threshold_band.json")
+    for case in fx["cases"]:
+        got = oracle.within_threshold_band(np.array(case["score"]), case["t"], case["rel"], case["abs_floor"])
+        assert got.tolist() == case["in_band"], (case["what"], got.tolist())
+    bc = fx["broadcast"]
+    got = oracle.within_threshold_band(np.array(bc["score"]), np.array(bc["t"]), bc["rel"], np.array(bc["abs_floor"]))
+    assert got.shape == (2, 3) and got.tolist() == bc["in_band"], got.tolist()
+    # default rel is the contract's 1e-3
+    assert oracle.within_threshold_band(1001.0, 1000.0) and not oracle.within_threshold_band(1001.0005, 1000.0)
+
+
 def pin_asymmetric_shapes():
     """f != d with a non-symmetric Dt: y = sum_i h_i Dt[i] (rows of Dt are neurons)."""
     Wg = np.array([[1.0, 0.0, 0.0], [0.0, 2.0, 0.0]])  # f = 2, d = 3

@@ -121,6 +121,26 @@ def _bf16_wrong_shift(bits):
     return (b.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
 
 
+def _band_rel_of_score(score, t, rel=1e-3, abs_floor=0.0):
+    s, t = np.asarray(score, float), np.asarray(t, float)
+    return np.abs(s - t) <= rel * np.abs(s) + abs_floor
+
+
+def _band_strict(score, t, rel=1e-3, abs_floor=0.0):
+    s, t = np.asarray(score, float), np.asarray(t, float)
+    return np.abs(s - t) < rel * np.abs(t) + abs_floor
+
+
+def _band_no_floor(score, t, rel=1e-3, abs_floor=0.0):
+    s, t = np.asarray(score, float), np.asarray(t, float)
+    return np.abs(s - t) <= rel * np.abs(t)
+
+
+def _band_signed_t(score, t, rel=1e-3, abs_floor=0.0):
+    s, t = np.asarray(score, float), np.asarray(t, float)
+    return np.abs(s - t) <= rel * t + abs_floor
+
+
 MUTATIONS = {
     "silu_sign": [(offn, "silu", _silu_wrong_sign)],
     "gate_bias_dropped": [(offn, "gate_up", _gate_up_no_bias), (osvd, "gate_up", _gate_up_no_bias)],
@@ -144,6 +164,14 @@ MUTATIONS = {
     "auc_classes_swapped": [(odia, "roc_auc", _auc_reference_swapped), (oracle, "roc_auc", _auc_reference_swapped)],
     "recall_as_precision": [(odia, "recall", _recall_as_precision), (oracle, "recall", _recall_as_precision)],
     "down_transposed": [(offn, "dense_ffn", _dense_ffn_transposed), (oracle, "dense_ffn", _dense_ffn_transposed)],
+    "band_relative_to_score": [(offn, "within_threshold_band", _band_rel_of_score),
+                               (oracle, "within_threshold_band", _band_rel_of_score)],
+    "band_strict_edge": [(offn, "within_threshold_band", _band_strict),
+                         (oracle, "within_threshold_band", _band_strict)],
+    "band_floor_dropped": [(offn, "within_threshold_band", _band_no_floor),
+                           (oracle, "within_threshold_band", _band_no_floor)],
+    "band_signed_threshold": [(offn, "within_threshold_band", _band_signed_t),
+                              (oracle, "within_threshold_band", _band_signed_t)],
     "bf16_decode_shift": [(offn, "bf16_to_f64", _bf16_wrong_shift), (oracle, "bf16_to_f64", _bf16_wrong_shift)],
 }
 
