@@ -45,6 +45,46 @@ def normwise_err(y, yhat):
     return float(np.max(np.abs(y - yhat)) / den) if den > 0 else float(np.max(np.abs(y)))
 
 
+# fp32 accumulation bound of the sparse paths (everything but the dense chunk, which
+# rounds its intermediate to bf16 for the matrix cores). Probabilistic rounding-error model
+# (each operation's relative error is at most u = 2^-24 and the errors are independent
+# and mean zero): a length-n sum in any order then errs by at most
+# LAMBDA u sqrt(n) ||terms||_2, except with probability below exp(-LAMBDA^2 / 2). Per
+# active row i: the gate and up dot products over d terms err by dg_i, du_i; h_i = act(g_i)
+# u_i inherits |act'| dg_i |u_i| + |a_i| du_i plus a few roundings of its own (the
+# exponential, the quotient, the product: ACT_ULPS u |h_i|); y_j = sum_i h_i Dt[i, j] then
+# errs by LAMBDA ||dh_i Dt[i, j]||_2 over the rows (independent row errors) plus its own
+# summation over the n rows. The bound is max_j of that over max_j |y_j|, normwise like
+# the tolerance. It sits about three orders of magnitude above the errors the kernels make
+# (~1e-7) and well below the 1e-2 contract, so a kernel that drops or repeats a row whose
+# term is not tiny fails it while the contract alone would let it pass.
+U32 = 2.0 ** -24
+LAMBDA = 8.0
+ACT_ULPS = 16.0
+
+
+def fp32_output_bound(Wg, Wu, Dt, x, mask, act="silu", b=None):
+    """Normwise fp32 accumulation bound of the masked FFN of one token (see above)."""
+    x = np.asarray(x, dtype=np.float64)
+    m = np.asarray(mask, dtype=bool)
+    if not m.any():
+        return 0.0
+    d, n = x.shape[0], int(m.sum())
+    Wg_m, Wu_m, Dt_m = Wg[m], Wu[m], Dt[m]
+    g, u = oracle.gate_up(Wg_m, Wu_m, x, None if b is None else np.asarray(b, dtype=np.float64)[m])
+    a = oracle.activation(act)(g)
+    h = a * u
+    x2 = x * x
+    dg = LAMBDA * U32 * np.sqrt(d) * np.sqrt((Wg_m * Wg_m) @ x2)
+    du = LAMBDA * U32 * np.sqrt(d) * np.sqrt((Wu_m * Wu_m) @ x2)
+    slope = 1.1 if act == "silu" else 1.0  # max |SiLU'| = 1.0998...
+    dh = slope * dg * np.abs(u) + np.abs(a) * du + ACT_ULPS * U32 * np.abs(h)
+    D2 = Dt_m * Dt_m
+    dy = LAMBDA * np.sqrt((dh * dh) @ D2) + LAMBDA * U32 * np.sqrt(n) * np.sqrt((h * h) @ D2)
+    ymax = np.max(np.abs(Dt_m.T @ h))
+    return float(np.max(dy) / ymax) if ymax > 0 else float(np.max(dy))
+
+
 def check_mask(gpu_mask, ora_mask, score, t, abs_band=0.0, what="mask"):
     """Masks must agree except where |score - t| <= BAND_REL |t| + abs_band; such
     mismatches may make up at most MAX_MISMATCH_FRAC of the neurons."""

@@ -5,7 +5,9 @@ Each case draws seeded synthetic inputs, runs the library through the C ABI and 
     threshold, at most 0.1% of the neurons;
   * outputs on the oracle's own mask (passed in as the mask override): normwise error
     <= 2e-3 (fp32 weights) / 1e-2 (bf16 weights), fp32 accumulation;
-  * outputs on the library's own mask against the oracle on that same mask.
+  * outputs on the library's own mask against the oracle on that same mask;
+  * both outputs also within the fp32 accumulation bound of tests.helpers, far below the
+    contract, so that a dropped or repeated row fails even where 1e-2 would pass it.
 """
 
 import numpy as np
@@ -14,7 +16,7 @@ import torch
 
 import oracle
 from contextual_activation_sparsity_amd import inputs
-from tests.helpers import (TOL_BF16, TOL_F32, check_mask, mask_from_idx, normwise_err, say,
+from tests.helpers import (TOL_BF16, TOL_F32, check_mask, fp32_output_bound, mask_from_idx, normwise_err, say,
                            swiglu_layer_dev, to_dev, to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -75,14 +77,15 @@ def _case(w, d, f, k, n_tok, seed_layer=0, batch=1, act="silu"):
             # own mask: compare with the oracle on the library's mask
             y_own = oracle.masked_ffn(Wg, Wu, Dt, xb[b], gm, act)
             e1 = normwise_err(y[b], y_own)
-            assert e1 <= tol, (j0 + b, e1)
+            bnd = fp32_output_bound(Wg, Wu, Dt, xb[b], gm, act)
+            assert e1 <= min(tol, bnd), (j0 + b, e1, bnd)
             worst = max(worst, e1)
         # oracle's mask through the override
         y2, idx2, n2 = run_decode(layer, xd, t, ws, mask=om.astype(np.uint8))
         for b in range(xb.shape[0]):
             yo = oracle.masked_ffn(Wg, Wu, Dt, xb[b], om[b], act)
             e2 = normwise_err(y2[b], yo)
-            assert e2 <= tol, (j0 + b, e2)
+            assert e2 <= min(tol, fp32_output_bound(Wg, Wu, Dt, xb[b], om[b], act)), (j0 + b, e2)
             assert n2[b] == om[b].sum()
             assert np.array_equal(np.sort(idx2[b][:n2[b]]), np.flatnonzero(om[b]))
     say(f"    worst normwise err {worst:.3e}, band mismatches {mism}")
