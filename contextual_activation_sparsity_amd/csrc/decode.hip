@@ -346,8 +346,9 @@ struct GateKernel {
 
   // rec(slot, row, activations, bits) is called by wave 0 for every selected row, slot
   // being its position in the tile's slice; returns the tile's selected-row count and
-  // where its slice of the lists starts.
-  template <class Rec>
+  // where its slice of the lists starts. LOCAL: the workgroup streams the up/down rows of
+  // its own list, kept in LDS by rec, so the global list is not written.
+  template <bool LOCAL, class Rec>
   __device__ static int2 run(const DecodeArgs& args, Rec&& rec) {
     const DevArgs a = dev_args(args);
     __shared__ Smem sm;
@@ -428,12 +429,14 @@ struct GateKernel {
         const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(ub >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ub, 0));
         const int q0 = sm.qlen;
         if (bits != 0) {
-          const int o = r0 + q0 + pos;  // this tile's slice of the global lists
-          a.sel_idx[o] = grow;
-          a.sel_bits[o] = (uint8_t)bits;
+          if constexpr (!LOCAL) {
+            const int o = r0 + q0 + pos;  // this tile's slice of the global lists
+            a.sel_idx[o] = grow;
+            a.sel_bits[o] = (uint8_t)bits;
 #pragma unroll
-          for (int b = 0; b < BMAX; ++b)
-            if (b < nb) a.sel_a[(size_t)b * a.f + o] = av[b];
+            for (int b = 0; b < BMAX; ++b)
+              if (b < nb) a.sel_a[(size_t)b * a.f + o] = av[b];
+          }
           rec(q0 + pos, grow, av, bits);
         }
         if (want_idx) {
@@ -467,17 +470,26 @@ struct GateKernel {
       }
       return sd;
     };
+    // Two steps per iteration and no exit inside the body: the loop then has a single
+    // path back to its head, along which exactly the loads of buffer a are in flight, so
+    // the compiler's wait counts let buffer b's loads go out while a's are still on their
+    // way. (An exit after the first half gave the head a second incoming path with b's
+    // loads in flight, and the head then waited for the older loads before issuing: one
+    // step in flight instead of two for much of every iteration.) An even step count ends
+    // with one issue of an empty step (loads of x, unused); an odd one processes its last
+    // step after the loop.
     StepDesc sa = step(0);
     issue(a, sm, sa, r0, nrows, cand_mode, rl, cl, lane, a0, a1, abias, amask);
-    for (int s = 0; s < ngate; s += 2) {
+    int s = 0;
+    for (; s + 1 < ngate; s += 2) {
       const StepDesc sb = step(s + 1);
       issue(a, sm, sb, r0, nrows, cand_mode, rl, cl, lane, b0, b1, bbias, bmask);
       process(sa, a0, a1, abias, amask);
-      if (s + 1 >= ngate) break;
       sa = step(s + 2);
       issue(a, sm, sa, r0, nrows, cand_mode, rl, cl, lane, a0, a1, abias, amask);
       process(sb, b0, b1, bbias, bmask);
     }
+    if (s < ngate) process(sa, a0, a1, abias, amask);
     if (tid < kCnt) {
       int v = 0;
       if (tid == 0) v = sm.qlen;
@@ -815,14 +827,15 @@ struct UpDownKernel {
         }
         return sd;
       };
+      // (the loop shape of the gate: no exit inside the body; see GateKernel::run)
       StepDesc sa = step(0);
       issue(a, sm, sa, lim, rl, cl, a0, a1);
-      for (int s = 0; s < nstep; s += 2) {
+      int s = 0;
+      for (; s + 1 < nstep; s += 2) {
         const StepDesc sb = step(s + 1);
         issue(a, sm, sb, lim, rl, cl, b0, b1);
         process(sa, a0, a1);
         if (balanced && s == 0) bal.load_counts(a);
-        if (s + 1 >= nstep) break;
         sa = step(s + 2);
         issue(a, sm, sa, lim, rl, cl, a0, a1);
         process(sb, b0, b1);
@@ -831,6 +844,7 @@ struct UpDownKernel {
           nstep = kPre + (max(lim - covered, 0) + RG - 1) / RG;
         }
       }
+      if (s < nstep) process(sa, a0, a1);
 
       // ---- partial of y (read by the reduce kernel after this launch completes)
       if (bal.poisoned()) {
@@ -995,17 +1009,19 @@ struct ParKernel {
       }
       return sd;
     };
+    // (the loop shape of the gate: no exit inside the body; see GateKernel::run)
     StepDesc sa = step(0);
     issue(a, sm, sa, nq, rl, cl, ag, au, ad);
-    for (int st = 0; st < nstep; st += 2) {
+    int st = 0;
+    for (; st + 1 < nstep; st += 2) {
       const StepDesc sb = step(st + 1);
       issue(a, sm, sb, nq, rl, cl, bg, bu, bd);
       process(sa, ag, au, ad);
-      if (st + 1 >= nstep) break;
       sa = step(st + 2);
       issue(a, sm, sa, nq, rl, cl, ag, au, ad);
       process(sb, bg, bu, bd);
     }
+    if (st < nstep) process(sa, ag, au, ad);
 
     // ---- partial of y (read by the reduce kernel after this launch completes)
     SFN_GLOBAL float* prow = a.part + (size_t)(w * RPG + rl) * a.d;
@@ -1134,7 +1150,7 @@ struct ReduceKernel {
 
 template <int WT, int BMAX, int CPT, int TPR, int R>
 __global__ __launch_bounds__(kNT) void decode_gate_kernel(DecodeArgs a) {
-  GateKernel<WT, BMAX, CPT, TPR, R>::run(a, [](int, int, const auto&, uint32_t) {});
+  GateKernel<WT, BMAX, CPT, TPR, R>::template run<false>(a, [](int, int, const auto&, uint32_t) {});
 }
 
 // Balancer of the one-token up/down (flags non-null, G <= kBalMaxTiles, every tile
@@ -1286,7 +1302,7 @@ __global__ __launch_bounds__(kNT) void decode_gate_local_kernel(DecodeArgs args)
   static_assert(BMAX == 1, "one token");
   __shared__ typename UD::Smem usm;
   __shared__ BalSmem bsm;
-  const int2 go = GateKernel<WT, BMAX, CPT, TPR, RGATE>::run(
+  const int2 go = GateKernel<WT, BMAX, CPT, TPR, RGATE>::template run<true>(
       args, [&](int slot, int row, const auto& av, uint32_t bits) {
         usm.qrow[slot] = row;
         usm.qbits[slot] = (uint8_t)bits;
