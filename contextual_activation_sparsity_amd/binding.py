@@ -31,6 +31,8 @@ SFN_F32, SFN_BF16 = 0, 1
 SFN_ACT_SILU, SFN_ACT_RELU = 0, 1
 SFN_MAX_BATCH, SFN_MAX_CHUNK = 4, 16
 SFN_PIPE_SEQUENTIAL, SFN_PIPE_PARALLEL = 0, 1
+SFN_WORKSPACE_HEADER_BYTES, SFN_WORKSPACE_STATUS_OFFSET = 2048, 1024
+SFN_STATUS_BALANCER_TIMEOUT, SFN_STATUS_PREDICTOR_TIMEOUT = 1, 2
 
 EXPORTED = (
     "sparse_ffn_workspace_size",
@@ -179,6 +181,13 @@ def svd_predict_workspace_size(pred: SVDPredictor) -> int:
 
 def sparse_ffn_strerror(status: int) -> str:
     return _lib.sparse_ffn_strerror(int(status)).decode()
+
+
+def workspace_status(ws: torch.Tensor) -> int:
+    """The workspace status word (synchronises): 0, or the SFN_STATUS_* code of a bounded
+    device-side wait that gave up during a call on this workspace."""
+    off = SFN_WORKSPACE_STATUS_OFFSET
+    return int(ws[off:off + 4].view(torch.int32).item())
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

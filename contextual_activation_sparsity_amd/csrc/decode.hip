@@ -1210,14 +1210,15 @@ struct Balancer {
     (void)covered;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // Every tile is resident at once (G <= CU count), so the wait ends once all have been
-    // dispatched; kernels of other streams can only delay that. The bound (seconds) is a
-    // guard: a workgroup that reaches it poisons its partial, so y is NaN, not wrong.
+    // dispatched; kernels of other streams can only delay that. The bound (2^20 round
+    // trips, about a second) is a guard: a workgroup that reaches it poisons its partial,
+    // so y is NaN, not wrong, and sets the workspace status word.
     uint32_t v = cw;
     bool late = false;
     if (tid < G) {
       uint32_t spins = 0;
       while (!(v & kPublished)) {
-        if (++spins > (1u << 24)) {
+        if (++spins > (1u << 20)) {
           late = true;
           break;
         }
@@ -1226,18 +1227,11 @@ struct Balancer {
       }
     }
     gave_up = __syncthreads_or(late) != 0;
+    if (gave_up && tid == 0) st_through(a.flags + kWsStatusWord, kStatusBalancer);
     // a tile has at most kTMax rows; the clamp keeps every index below in bounds even if
     // the header held something other than zeros when the call started
     const int c = tid < G ? min((int)(v & ~kPublished), kTMax) : 0;
-    auto incl = [&](int x) {  // inclusive scan over the wave
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
-        const int u = __shfl_up(x, m, 64);
-        if (lane >= m) x += u;
-      }
-      return x;
-    };
-    const int ic = incl(c);
+    const int ic = wave_incl_scan(c);
     if (lane == 63) bs.wsum[0][wave] = ic;
     if (tid < G) bs.cnt[tid] = c;
     __syncthreads();
@@ -1248,7 +1242,7 @@ struct Balancer {
     const int kt = keep_of(c, T);
     const int ex = c - kt;                             // given away by tile tid
     const int df = tid < G ? max(T - kt, 0) : 0;       // taken by tile tid
-    const int ie = incl(ex), id = incl(df);
+    const int ie = wave_incl_scan(ex), id = wave_incl_scan(df);
     if (lane == 63) {
       bs.wsum[1][wave] = ie;
       bs.wsum[2][wave] = id;

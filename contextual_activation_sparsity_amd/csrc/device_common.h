@@ -145,6 +145,21 @@ __device__ __forceinline__ float group_sum(float v) {
 // Sum over all 64 lanes; every lane receives the total.
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
+// Inclusive prefix sum over the 64 lanes of a wave: each row of 16 lanes scans itself
+// with DPP right shifts by 1, 2, 4 and 8 (a lane with no source in its row adds 0), then
+// row_bcast:15 adds the last lane of row 0 / row 2 to rows 1 / 3 and row_bcast:31 adds
+// lane 31 (by then the total of rows 0 and 1) to rows 2 and 3. VALU moves only, no trip
+// through the LDS crossbar. The whole wave must be active.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
 // Lane select for the halving steps: hi in the lanes whose index has bit BIT set, lo in
 // the others, for BIT in {32, 16, 8, 4}. A DPP identity move whose row mask (lane groups
 // of 16) or bank mask (groups of 4 inside a row) enables only those lanes writes hi there

@@ -12,11 +12,16 @@ namespace sfn {
 // Workspace layout shared by every call on a workspace:
 //   [0, kWsHeader)      words that must be zero when a call starts: zero-filled once by
 //                       the caller, and every call that sets some clears them again in
-//                       its last launch (the one-token decode publishes its tiles' active
-//                       counts there for the balancer)
+//                       its last launch:
+//     words [0, 256)      the one-token decode's tile counts (balancer)
+//     word kWsStatusWord  status: 0, or the code of a bounded device wait that gave up
+//                         (left set for the caller to read; see sparse_ffn.h)
 //   [kWsHeader, ...)    per-call scratch, rewritten by each call before it is read
 // Scratch of one call may overlap scratch of another.
-constexpr size_t kWsHeader = 2048;
+constexpr size_t kWsHeader = SFN_WORKSPACE_HEADER_BYTES;
+constexpr int kWsStatusWord = SFN_WORKSPACE_STATUS_OFFSET / 4;
+constexpr uint32_t kStatusBalancer = SFN_STATUS_BALANCER_TIMEOUT;
+constexpr uint32_t kStatusPredictor = SFN_STATUS_PREDICTOR_TIMEOUT;
 
 struct DecodeArgs {
   const char* wg;

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(512) void svd_p_kernel(const char* __restrict__ l, 
                                                     const float* __restrict__ bias, const float* __restrict__ tau,
                                                     int f, int r, int32_t* __restrict__ cand, int32_t* n_cand,
                                                     float* __restrict__ p_out,
-                                                    unsigned long long* flags, int ntiles) {
+                                                    unsigned long long* flags, int ntiles, uint32_t* status) {
   constexpr int RPI = 512 / TPR;  // rows side by side
   constexpr int NIT = kRowsPerTile / RPI;
   constexpr int NCW = kRowsPerTile / 64;  // comparing waves
@@ -144,9 +144,14 @@ __global__ __launch_bounds__(512) void svd_p_kernel(const char* __restrict__ l, 
   // reads the counts of all lower tiles (four per lane in flight, waiting for any not yet
   // published: lower tiles have lower workgroup indices, so they are running) and sums
   // them. No tile waits on another tile's prefix, so there is no chain of round trips.
+  // The wait is bounded (2^20 round trips, about a second; never expected, since lower
+  // tiles always publish). A tile that gives up sets the workspace status word; the last
+  // tile waits on every other one, so it gives up too and reports n_cand = -1 instead of
+  // a count built from missing words.
   if (wave == 0) {
     if (lane == 0) __hip_atomic_store(&flags[tile], pack(1u, cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t excl = 0;
+    bool late = false;
     for (int b0 = 0; b0 < tile; b0 += 256) {
       uint32_t v = 0;
 #pragma unroll
@@ -157,7 +162,10 @@ __global__ __launch_bounds__(512) void svd_p_kernel(const char* __restrict__ l, 
           uint32_t spins = 0;
           while (((fl = __hip_atomic_load(&flags[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 32) == 0ull) {
             __builtin_amdgcn_s_sleep(1);
-            if (++spins > (1u << 24)) break;  // never expected: lower tiles always publish
+            if (++spins > (1u << 20)) {
+              late = true;
+              break;
+            }
           }
           v += (uint32_t)fl;
         }
@@ -166,9 +174,11 @@ __global__ __launch_bounds__(512) void svd_p_kernel(const char* __restrict__ l, 
       for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
       excl += v;
     }
+    const bool gave_up = __ballot(late) != 0ull;
     if (lane == 0) {
       s_excl = excl;
-      if (tile == ntiles - 1) *n_cand = (int32_t)(excl + cnt);
+      if (gave_up) __hip_atomic_store(status, kStatusPredictor, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tile == ntiles - 1) *n_cand = gave_up ? -1 : (int32_t)(excl + cnt);
     }
   }
   __syncthreads();
@@ -206,6 +216,7 @@ hipError_t launch_svd_predict(const sfn_svd& s, const void* x, int32_t* cand, in
   size_t off = (size_t)ntiles * sizeof(unsigned long long);
   off = (off + 255) & ~(size_t)255;
   float* z = reinterpret_cast<float*>(p + off);
+  uint32_t* status = reinterpret_cast<uint32_t*>(ws) + kWsStatusWord;
   hipLaunchKernelGGL(svd_z_kernel, dim3((s.r + 1) / 2), dim3(512), 0, stream, static_cast<const char*>(s.q),
                      static_cast<const char*>(x), s.d, s.r, z, flags, ntiles);
   hipError_t e = hipGetLastError();
@@ -214,7 +225,7 @@ hipError_t launch_svd_predict(const sfn_svd& s, const void* x, int32_t* cand, in
   const char* l = static_cast<const char*>(s.l);
 #define SFN_P_LAUNCH(TPR, CH)                                                                                      \
   hipLaunchKernelGGL((svd_p_kernel<TPR, CH>), dim3(ntiles), dim3(512), 0, stream, l, z, s.b, s.tau, s.f, s.r, cand, \
-                     n_cand, p_out, flags, ntiles)
+                     n_cand, p_out, flags, ntiles, status)
   if (nch <= 8) {
     SFN_P_LAUNCH(8, 1);
   } else if (nch <= 16) {

@@ -35,14 +35,21 @@
  *     which reports a launch error from the HIP runtime. Device-side faults surface at
  *     the caller's next synchronisation. No C++ exception crosses the ABI.
  *   - Workspace: `ws` of `ws_bytes` bytes (256-byte aligned), sized by the
- *     *_workspace_size queries. Its first 2 KiB are reserved and must be zero-filled
- *     once when the workspace is allocated (e.g. torch.zeros). A call may use them
- *     between its own kernels (the one-token decode publishes per-tile counts there)
- *     but its last kernel zeroes them again, so they are zero whenever no call is in
- *     flight. Everything after them is scratch each call rewrites before reading, so any
- *     sequence of calls on one stream may share one workspace (sized for the largest
- *     of them). Calls that may run concurrently (different streams) need distinct
- *     workspaces.
+ *     *_workspace_size queries. Its first SFN_WORKSPACE_HEADER_BYTES (2 KiB) are
+ *     reserved and must be zero-filled once when the workspace is allocated (e.g.
+ *     torch.zeros). A call may use them between its own kernels (the one-token decode
+ *     publishes per-tile counts there) but its last kernel zeroes them again, so they are
+ *     zero whenever no call is in flight. Everything after them is scratch each call
+ *     rewrites before reading, so any sequence of calls on one stream may share one
+ *     workspace (sized for the largest of them). Calls that may run concurrently
+ *     (different streams) need distinct workspaces.
+ *   - Status word: the uint32 at byte SFN_WORKSPACE_STATUS_OFFSET of the workspace stays
+ *     0 through every call that completes normally. The library's few device-side waits
+ *     (workgroups of one launch waiting for each other's results, which only a device
+ *     that never schedules some of them can stall) are bounded; one that gives up writes
+ *     its SFN_STATUS_* code there and that call's outputs are invalid (y is NaN, or
+ *     *n_cand is -1). The word stays set for the caller to read after a
+ *     synchronisation; zero the whole header again before the workspace is reused.
  *   - Outputs are deterministic: identical inputs give bitwise identical y, index
  *     lists and thresholds (fixed reduction orders, no floating-point atomics).
  *   - Arithmetic: products and sums in fp32 (bf16 inputs are widened exactly).
@@ -66,6 +73,12 @@ extern "C" {
 #define SFN_EALIGN (-5)       /* a pointer or a row not 16-byte aligned */
 #define SFN_EUNSUPPORTED (-6) /* valid request this library does not implement */
 #define SFN_EHIP (-7)         /* the HIP runtime reported an error on launch */
+
+/* Workspace header (see the conventions above). */
+#define SFN_WORKSPACE_HEADER_BYTES 2048
+#define SFN_WORKSPACE_STATUS_OFFSET 1024
+#define SFN_STATUS_BALANCER_TIMEOUT 1u  /* sparse_ffn_decode / _svd: the one-token tile balancer */
+#define SFN_STATUS_PREDICTOR_TIMEOUT 2u /* svd_predict: the scan over the tiles' counts */
 
 /* Weight (and token) dtypes. */
 #define SFN_F32 0
@@ -153,7 +166,8 @@ int sparse_ffn_calibrate(const sfn_ffn* ffn, const void* x_cal, int32_t n, float
  *   share out their up/down rows, so each waits until all of them have run their gate
  *   part. On a device with at least as many compute units as workgroups they are all
  *   resident at once; kernels on other streams can only delay them. Should the wait
- *   exceed several seconds, y comes out NaN rather than wrong.
+ *   exceed about a second, y comes out NaN rather than wrong and the workspace status
+ *   word reads SFN_STATUS_BALANCER_TIMEOUT.
  */
 int sparse_ffn_decode(const sfn_ffn* ffn, const void* x, int32_t B, const float* t,
                       const int32_t* cand, const int32_t* n_cand, const uint8_t* mask_in,
@@ -184,7 +198,8 @@ int sparse_ffn_decode_parallel(const sfn_ffn* ffn, const void* x, const int32_t*
  * {i : p_i > tau_i} written in ascending order.
  *   x        [d] bf16
  *   cand_idx [f] int32 (device), the first *n_cand entries written
- *   n_cand   1 int32 (device)
+ *   n_cand   1 int32 (device); -1 if the tiles' count exchange timed out (then the
+ *            workspace status word reads SFN_STATUS_PREDICTOR_TIMEOUT; see the conventions)
  *   p_out    [f] fp32 (device) or NULL: the predictions
  */
 int svd_predict(const sfn_svd* svd, const void* x, int32_t* cand_idx, int32_t* n_cand,

@@ -42,6 +42,24 @@ def test_library_exports_every_declared_symbol():
     assert set(B.EXPORTED) == set(declared_functions())
 
 
+def header_defines():
+    return dict(re.findall(r"^#define\s+(SFN_[A-Z0-9_]+)\s+\(?(-?\d+)u?\)?", open(HEADER).read(), flags=re.M))
+
+
+@needs_lib
+def test_binding_constants_match_the_header():
+    """Every constant the binding mirrors has the header's value (status codes, dtypes,
+    limits, the workspace header layout and its status codes)."""
+    defs = header_defines()
+    names = [n for n in dir(B) if n.startswith("SFN_") and isinstance(getattr(B, n), int)]
+    assert len(names) >= 20
+    for n in names:
+        assert n in defs, f"{n} is not defined in the header"
+        assert getattr(B, n) == int(defs[n]), (n, getattr(B, n), defs[n])
+    # the status word sits inside the reserved header, after the 256 tile count words
+    assert 256 * 4 <= B.SFN_WORKSPACE_STATUS_OFFSET < B.SFN_WORKSPACE_HEADER_BYTES
+
+
 @needs_lib
 def test_strerror_covers_codes():
     for code in range(0, -8, -1):

@@ -31,7 +31,7 @@ def _tol(dtype):
 
 def _header_clear(ws):
     """The first 2 KiB of a workspace are reserved: zero whenever no call is in flight."""
-    return not bool(ws[:2048].any().item())
+    return not bool(ws[:B.SFN_WORKSPACE_HEADER_BYTES].any().item())
 
 
 def run_decode(layer, x_dev, t_val, ws, mask=None, want_y=True, cand=None, n_cand=None):

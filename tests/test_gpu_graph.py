@@ -88,7 +88,7 @@ def test_graph_replays_match_eager():
         del junk
         for k, v in out.items():
             assert torch.equal(v, ref[k]), f"replay {rep}: {k} differs from the eager result"
-        assert not bool(ws[:2048].any().item())
+        assert not bool(ws[:B.SFN_WORKSPACE_HEADER_BYTES].any().item())
 
 
 def test_graph_replays_balanced_one_token():
@@ -135,4 +135,4 @@ def test_graph_replays_balanced_one_token():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(Y, ref[0]) and torch.equal(I, ref[1]) and torch.equal(N, ref[2]), rep
-        assert not bool(ws[:2048].any().item())
+        assert not bool(ws[:B.SFN_WORKSPACE_HEADER_BYTES].any().item())

@@ -73,7 +73,7 @@ def _run(layer, pred, xd, pipeline, want_y=True):
     n = torch.full((1,), -1, dtype=torch.int32, device="cuda")
     B.sparse_ffn_decode_svd(layer, pred, xd, ws, y=y, idx=idx, n_idx=n, pipeline=pipeline)
     torch.cuda.synchronize()
-    assert not bool(ws[:2048].any().item()), "reserved workspace header changed"
+    assert not bool(ws[:B.SFN_WORKSPACE_HEADER_BYTES].any().item()), "reserved workspace header changed"
     nn = int(n.item())
     ii = idx.cpu().numpy()
     assert 0 <= nn <= f and np.all(np.diff(ii[:nn]) > 0), "ascending rows"
