@@ -26,13 +26,14 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 SFN_OK, SFN_EINVAL, SFN_ESHAPE, SFN_EDTYPE = 0, -1, -2, -3
-SFN_EWORKSPACE, SFN_EALIGN, SFN_EUNSUPPORTED, SFN_EHIP = -4, -5, -6, -7
+SFN_EWORKSPACE, SFN_EALIGN, SFN_EUNSUPPORTED, SFN_EHIP, SFN_ETOOLARGE = -4, -5, -6, -7, -8
 SFN_F32, SFN_BF16 = 0, 1
 SFN_ACT_SILU, SFN_ACT_RELU = 0, 1
 SFN_MAX_BATCH, SFN_MAX_CHUNK = 4, 16
 SFN_PIPE_SEQUENTIAL, SFN_PIPE_PARALLEL = 0, 1
 SFN_WORKSPACE_HEADER_BYTES, SFN_WORKSPACE_STATUS_OFFSET = 2048, 1024
 SFN_STATUS_BALANCER_TIMEOUT, SFN_STATUS_PREDICTOR_TIMEOUT = 1, 2
+SFN_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTED = (
     "sparse_ffn_workspace_size",
@@ -40,6 +41,7 @@ EXPORTED = (
     "sparse_ffn_strerror",
     "sparse_ffn_calibrate",
     "sparse_ffn_decode",
+    "sparse_ffn_decode_noalloc",
     "sparse_ffn_decode_parallel",
     "sparse_ffn_svd_workspace_size",
     "sparse_ffn_decode_svd",
@@ -74,6 +76,8 @@ _lib.sparse_ffn_calibrate.argtypes = [ctypes.POINTER(sfn_ffn), _vp, _i32, _f32, 
 _lib.sparse_ffn_calibrate.restype = ctypes.c_int
 _lib.sparse_ffn_decode.argtypes = [ctypes.POINTER(sfn_ffn), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.sparse_ffn_decode.restype = ctypes.c_int
+_lib.sparse_ffn_decode_noalloc.argtypes = [ctypes.POINTER(sfn_ffn), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.sparse_ffn_decode_noalloc.restype = ctypes.c_int
 _lib.sparse_ffn_decode_parallel.argtypes = [ctypes.POINTER(sfn_ffn), _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.sparse_ffn_decode_parallel.restype = ctypes.c_int
 _lib.sparse_ffn_svd_workspace_size.argtypes = [ctypes.POINTER(sfn_ffn), ctypes.POINTER(sfn_svd)]
@@ -221,6 +225,21 @@ def sparse_ffn_decode(layer: FFNLayer, x: torch.Tensor, t: Optional[torch.Tensor
         _ptr(active_idx, "active_idx", torch.int32, B * layer.f), _ptr(n_active, "n_active", torch.int32, B),
         _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "sparse_ffn_decode")
+
+
+def sparse_ffn_decode_noalloc(layer: FFNLayer, x: torch.Tensor, t: Optional[torch.Tensor],
+                              y: Optional[torch.Tensor] = None, cand: Optional[torch.Tensor] = None,
+                              n_cand: Optional[torch.Tensor] = None, mask_in: Optional[torch.Tensor] = None,
+                              active_idx: Optional[torch.Tensor] = None, n_active: Optional[torch.Tensor] = None,
+                              stream=None):
+    B = x.shape[0] if x.dim() == 2 else 1
+    st = _lib.sparse_ffn_decode_noalloc(
+        ctypes.byref(layer.c), _ptr(x, "x", layer.dtype, B * layer.d), int(B),
+        _ptr(t, "t", torch.float32, 1), _ptr(cand, "cand", torch.int32), _ptr(n_cand, "n_cand", torch.int32, 1),
+        _ptr(mask_in, "mask_in", torch.uint8, B * layer.f), _ptr(y, "y", torch.float32, B * layer.d),
+        _ptr(active_idx, "active_idx", torch.int32, B * layer.f), _ptr(n_active, "n_active", torch.int32, B),
+        _stream(stream))
+    _check(st, "sparse_ffn_decode_noalloc")
 
 
 def sparse_ffn_decode_parallel(layer: FFNLayer, x: torch.Tensor, cand: torch.Tensor, n_cand: torch.Tensor,

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <exception>
@@ -55,6 +56,79 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SFN_OK : SFN_EHIP; }
 
+// Validation and launch of one decode step on a workspace (sparse_ffn_decode and its
+// allocation-free variant).
+int decode_validate(const sfn_ffn* ffn, const void* x, int32_t B, const float* t, const int32_t* cand,
+                    const int32_t* n_cand, const uint8_t* mask_in, float* y) {
+  const int st = check_ffn(ffn, y != nullptr);
+  if (st != SFN_OK) return st;
+  if (!x) return SFN_EINVAL;
+  if (!aligned16(x)) return SFN_EALIGN;
+  if (B < 1 || B > SFN_MAX_BATCH) return SFN_ESHAPE;
+  if ((cand == nullptr) != (n_cand == nullptr)) return SFN_EINVAL;
+  if (cand && (B != 1 || mask_in)) return SFN_EINVAL;
+  if (y && !aligned16(y)) return SFN_EALIGN;
+  if (t && (reinterpret_cast<uintptr_t>(t) & 3u)) return SFN_EALIGN;
+  return SFN_OK;
+}
+
+size_t decode_need(const sfn_ffn* ffn, int32_t B) {
+  return sfn::decode_workspace_bytes(ffn->d, ffn->f, wbytes(ffn->wdtype), B > 1 ? SFN_MAX_BATCH : 1);
+}
+
+int decode_launch(const sfn_ffn* ffn, const void* x, int32_t B, const float* t, const int32_t* cand,
+                  const int32_t* n_cand, const uint8_t* mask_in, float* y, int32_t* active_idx, int32_t* n_active,
+                  void* ws, void* stream) {
+  const int wb = wbytes(ffn->wdtype);
+  sfn::DecodeArgs a{};
+  a.wg = static_cast<const char*>(ffn->w_gate);
+  a.wu = static_cast<const char*>(ffn->w_up);
+  a.wd = static_cast<const char*>(ffn->w_down_t);
+  a.bias = ffn->b_gate;
+  a.x = static_cast<const char*>(x);
+  a.t = t;
+  a.cand = cand;
+  a.n_cand = n_cand;
+  a.mask_in = mask_in;
+  a.y = y;
+  a.active_idx = active_idx;
+  a.n_active = n_active;
+  a.d = ffn->d;
+  a.f = ffn->f;
+  a.nch = ffn->d * wb / 16;
+  a.row_bytes = ffn->d * wb;
+  a.nb = B;
+  a.act = ffn->act;
+  a.G = sfn::decode_grid(ffn->f);
+  a.n_red = sfn::decode_reducers(a.G, B, ffn->d);
+  sfn::decode_carve(a, ws, wb);
+  return hip_status(sfn::launch_decode(a, ffn->wdtype, static_cast<hipStream_t>(stream)));
+}
+
+// Scratch of sparse_ffn_decode_noalloc: a file-scope device array, one copy on each GPU
+// the library runs on, zero when the code object is loaded. Kernels never see its name:
+// host code takes its device address from hipGetSymbolAddress, once per device with that
+// device current, and passes that address like a workspace.
+constexpr size_t kNoAllocScratchBytes = SFN_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (resolved on the first call on each device;
+// host threads that race store the same value).
+int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SFN_EHIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SFN_EHIP;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return SFN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -94,6 +168,8 @@ const char* sparse_ffn_strerror(int status) {
     case SFN_EALIGN: return "pointer or row not 16-byte aligned (workspace: 256-byte)";
     case SFN_EUNSUPPORTED: return "request not implemented by this library";
     case SFN_EHIP: return "HIP runtime error on launch";
+    case SFN_ETOOLARGE:
+      return "request needs more scratch than sparse_ffn_decode_noalloc's fixed array (SFN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -102,43 +178,27 @@ int sparse_ffn_decode(const sfn_ffn* ffn, const void* x, int32_t B, const float*
                       const int32_t* n_cand, const uint8_t* mask_in, float* y, int32_t* active_idx,
                       int32_t* n_active, void* ws, size_t ws_bytes, void* stream) {
   try {
-    int st = check_ffn(ffn, y != nullptr);
+    int st = decode_validate(ffn, x, B, t, cand, n_cand, mask_in, y);
     if (st != SFN_OK) return st;
-    if (!x) return SFN_EINVAL;
-    if (!aligned16(x)) return SFN_EALIGN;
-    if (B < 1 || B > SFN_MAX_BATCH) return SFN_ESHAPE;
-    if ((cand == nullptr) != (n_cand == nullptr)) return SFN_EINVAL;
-    if (cand && (B != 1 || mask_in)) return SFN_EINVAL;
-    if (y && !aligned16(y)) return SFN_EALIGN;
-    if (t && (reinterpret_cast<uintptr_t>(t) & 3u)) return SFN_EALIGN;
-    const int wb = wbytes(ffn->wdtype);
-    const int nb = B > 1 ? SFN_MAX_BATCH : 1;
-    st = check_ws(ws, ws_bytes, sfn::decode_workspace_bytes(ffn->d, ffn->f, wb, nb));
+    st = check_ws(ws, ws_bytes, decode_need(ffn, B));
     if (st != SFN_OK) return st;
+    return decode_launch(ffn, x, B, t, cand, n_cand, mask_in, y, active_idx, n_active, ws, stream);
+  } catch (...) {
+    return SFN_EHIP;
+  }
+}
 
-    sfn::DecodeArgs a{};
-    a.wg = static_cast<const char*>(ffn->w_gate);
-    a.wu = static_cast<const char*>(ffn->w_up);
-    a.wd = static_cast<const char*>(ffn->w_down_t);
-    a.bias = ffn->b_gate;
-    a.x = static_cast<const char*>(x);
-    a.t = t;
-    a.cand = cand;
-    a.n_cand = n_cand;
-    a.mask_in = mask_in;
-    a.y = y;
-    a.active_idx = active_idx;
-    a.n_active = n_active;
-    a.d = ffn->d;
-    a.f = ffn->f;
-    a.nch = ffn->d * wb / 16;
-    a.row_bytes = ffn->d * wb;
-    a.nb = B;
-    a.act = ffn->act;
-    a.G = sfn::decode_grid(ffn->f);
-    a.n_red = sfn::decode_reducers(a.G, B, ffn->d);
-    sfn::decode_carve(a, ws, wb);
-    return hip_status(sfn::launch_decode(a, ffn->wdtype, static_cast<hipStream_t>(stream)));
+int sparse_ffn_decode_noalloc(const sfn_ffn* ffn, const void* x, int32_t B, const float* t, const int32_t* cand,
+                              const int32_t* n_cand, const uint8_t* mask_in, float* y, int32_t* active_idx,
+                              int32_t* n_active, void* stream) {
+  try {
+    int st = decode_validate(ffn, x, B, t, cand, n_cand, mask_in, y);
+    if (st != SFN_OK) return st;
+    if (decode_need(ffn, B) > kNoAllocScratchBytes) return SFN_ETOOLARGE;
+    void* ws = nullptr;
+    st = scratch_ptr(&ws);
+    if (st != SFN_OK) return st;
+    return decode_launch(ffn, x, B, t, cand, n_cand, mask_in, y, active_idx, n_active, ws, stream);
   } catch (...) {
     return SFN_EHIP;
   }

@@ -73,12 +73,14 @@ extern "C" {
 #define SFN_EALIGN (-5)       /* a pointer or a row not 16-byte aligned */
 #define SFN_EUNSUPPORTED (-6) /* valid request this library does not implement */
 #define SFN_EHIP (-7)         /* the HIP runtime reported an error on launch */
+#define SFN_ETOOLARGE (-8)    /* sparse_ffn_decode_noalloc: more scratch than its fixed array */
 
 /* Workspace header (see the conventions above). */
 #define SFN_WORKSPACE_HEADER_BYTES 2048
 #define SFN_WORKSPACE_STATUS_OFFSET 1024
 #define SFN_STATUS_BALANCER_TIMEOUT 1u  /* sparse_ffn_decode / _svd: the one-token tile balancer */
 #define SFN_STATUS_PREDICTOR_TIMEOUT 2u /* svd_predict: the scan over the tiles' counts */
+#define SFN_NOALLOC_SCRATCH_BYTES 33554432 /* fixed scratch of sparse_ffn_decode_noalloc */
 
 /* Weight (and token) dtypes. */
 #define SFN_F32 0
@@ -173,6 +175,27 @@ int sparse_ffn_decode(const sfn_ffn* ffn, const void* x, int32_t B, const float*
                       const int32_t* cand, const int32_t* n_cand, const uint8_t* mask_in,
                       float* y, int32_t* active_idx, int32_t* n_active, void* ws,
                       size_t ws_bytes, void* stream);
+
+/*
+ * sparse_ffn_decode without a workspace, for callers that cannot allocate or hand over
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The same arguments (minus ws and ws_bytes), checks and results as
+ * sparse_ffn_decode. The step's scratch is a fixed device array of
+ * SFN_NOALLOC_SCRATCH_BYTES (32 MiB) inside the library, one on each GPU it runs on, held
+ * until the process ends; the call allocates nothing. It holds the scratch of one-token
+ * calls up to f = 65536 at any d (e.g. d 8192, f 28672: 9 MiB) and of batches of up to
+ * four tokens at d <= 4096, f <= 65536; a call that needs more returns SFN_ETOOLARGE
+ * before anything is enqueued.
+ * The array is shared by every call on one GPU and keeps the last call's contents: each
+ * call leaves its reserved first SFN_WORKSPACE_HEADER_BYTES zero again, as
+ * sparse_ffn_decode leaves a workspace, so calls in order on one stream (or with a
+ * synchronisation between them) are safe. Calls that can overlap on one GPU (different
+ * streams, or several host threads) race on the array and give wrong results. A bounded
+ * wait that gives up shows as NaN in y (the array's status word is not exposed).
+ */
+int sparse_ffn_decode_noalloc(const sfn_ffn* ffn, const void* x, int32_t B, const float* t,
+                              const int32_t* cand, const int32_t* n_cand, const uint8_t* mask_in,
+                              float* y, int32_t* active_idx, int32_t* n_active, void* stream);
 
 /*
  * Candidate rows in one pass for one token: the SVD predictor's parallel pipeline ("SVD

@@ -62,7 +62,7 @@ def test_binding_constants_match_the_header():
 
 @needs_lib
 def test_strerror_covers_codes():
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = B.sparse_ffn_strerror(code)
         assert s and s != "unknown status"
     assert B.sparse_ffn_strerror(-99) == "unknown status"
@@ -126,6 +126,35 @@ def test_decode_validation():
     assert call(ffn=ctypes.byref(_ffn(wg=FAKE + 2))) == B.SFN_EALIGN
     # batch 4 needs the larger workspace
     assert call(B=4, x=FAKE) == B.SFN_EWORKSPACE
+
+
+@needs_lib
+def test_decode_noalloc_validation():
+    """The allocation-free decode checks its arguments like sparse_ffn_decode and rejects
+    a request whose scratch exceeds its fixed array with SFN_ETOOLARGE, all before any
+    HIP call (a valid request would resolve the array's device address, so none is made
+    here)."""
+    lib = B.raw()
+    ffn = _ffn()
+    call = lambda **kw: lib.sparse_ffn_decode_noalloc(  # noqa: E731
+        kw.get("ffn", ctypes.byref(ffn)), kw.get("x", FAKE), kw.get("B", 1), kw.get("t", FAKE),
+        kw.get("cand", None), kw.get("n_cand", None), kw.get("mask", None), kw.get("y", FAKE),
+        kw.get("idx", None), kw.get("n_act", None), None)
+    assert call(ffn=None) == B.SFN_EINVAL
+    assert call(x=None) == B.SFN_EINVAL
+    assert call(x=FAKE + 4) == B.SFN_EALIGN
+    assert call(B=0) == B.SFN_ESHAPE
+    assert call(B=5) == B.SFN_ESHAPE
+    assert call(cand=FAKE) == B.SFN_EINVAL
+    assert call(cand=FAKE, n_cand=FAKE, B=2) == B.SFN_EINVAL
+    assert call(y=FAKE + 8) == B.SFN_EALIGN
+    assert call(ffn=ctypes.byref(_ffn(wdtype=3))) == B.SFN_EDTYPE
+    # four tokens at d 8192 need 32 MiB of partials alone, more than the fixed array;
+    # so does one token at f 262144 (1024 tiles of 64 KB partials at d 16384)
+    big = _ffn(d=8192, f=28672)
+    assert call(ffn=ctypes.byref(big), B=4) == B.SFN_ETOOLARGE
+    assert call(ffn=ctypes.byref(_ffn(d=16384, f=262144)), B=1) == B.SFN_ETOOLARGE
+    assert "noalloc" in B.sparse_ffn_strerror(B.SFN_ETOOLARGE)
 
 
 @needs_lib
