@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other workloads (batch 4, SVD pipeline, 70B-shape decode and 16-token chunk)")
+    ap.add_argument("--legs", default=",".join(EXTRA_LEGS),
+                    help="comma list of the other workloads to run: " + ", ".join(EXTRA_LEGS))
     ap.add_argument("--no-table4", action="store_true",
                     help="skip the fixed-sparsity protocol (random candidate subsets on every layer, three shapes)")
     ap.add_argument("--no-quality", action="store_true",
@@ -295,11 +297,16 @@ def time_mixed(torch, steps, mode):
     return e0.elapsed_time(e1)
 
 
-def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4):
+EXTRA_LEGS = ("tiny", "b4", "b1", "70b", "chunk", "sirius", "svd")
+
+
+def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4, legs=EXTRA_LEGS, svd_layers=32,
+           svd_prepared=4):
     """The other workloads, each timed like the headline (graphs of per-layer calls, HIP
     events over the timed steps) on n_layers independently seeded layers: per-call time,
     algorithmic bytes and GB/s. Inputs as in the headline: on-device Gaussian weights,
-    x ~ N(0, I) in bf16, thresholds from the library's own calibration."""
+    x ~ N(0, I) in bf16, thresholds from the library's own calibration. `legs` picks a
+    subset (for profiling one workload at a time)."""
     import numpy as np
     lib = B.raw()
     dev = "cuda"
@@ -365,214 +372,287 @@ def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4):
         del layers, ws, X, y
         torch.cuda.empty_cache()
 
-    # batch of 4 with per-token masks and the union gather (Llama-3-8B shape), and batch 1
-    w2 = inputs.workload(2)
-    decode_leg("llama3_8b_b4_k50", w2, w2.d, w2.f, 4, 0.5, n_layers)
-    decode_leg("llama3_8b_b1_k50", w2, w2.d, w2.f, 1, 0.5, n_layers)
-    decode_leg("llama3_8b_b4_k60", w2, w2.d, w2.f, 4, 0.6, n_layers)
-    decode_leg("llama3_8b_b1_k60", w2, w2.d, w2.f, 1, 0.6, n_layers)
-    # sparse decode at the Llama-3-70B shape (d 8192: two 16-byte chunks per thread)
-    w4 = inputs.workload(4)
-    decode_leg("llama3_70b_b1_k50", w4, w4.d, w4.f, 1, 0.5, 2)
+    def chunk_leg(w4):
+        # 16-token dense verification chunk at the Llama-3-70B shape
+        layers = swiglu_layers(w4, w4.d, w4.f, 2)
+        ws = B.workspace(B.sparse_ffn_workspace_size(layers[0], 16))
+        X = xtok(w4, (n_warm + n_steps, 2, 16, w4.d), inputs.STREAM_DECODE)
+        Y = torch.zeros((2, 16, w4.d), dtype=torch.float32, device=dev)
+        wsp, wsb = ws.data_ptr(), ws.numel()
 
-    # 16-token dense verification chunk at the Llama-3-70B shape
-    layers = swiglu_layers(w4, w4.d, w4.f, 2)
-    ws = B.workspace(B.sparse_ffn_workspace_size(layers[0], 16))
-    X = xtok(w4, (n_warm + n_steps, 2, 16, w4.d), inputs.STREAM_DECODE)
-    Y = torch.zeros((2, 16, w4.d), dtype=torch.float32, device=dev)
-    wsp, wsb = ws.data_ptr(), ws.numel()
+        def chunk(tok, l):
+            return (lib.ffn_dense_chunk, (ctypes.byref(layers[l].c), X[tok, l].data_ptr(), 16, Y[l].data_ptr(), wsp, wsb))
+        time_mixed(torch, [[chunk(tok, l) for l in range(2)] for tok in range(n_warm)], mode)
+        ms = time_mixed(torch, [[chunk(tok, l) for l in range(2)] for tok in range(n_warm, n_warm + n_steps)], mode)
+        us = ms * 1e3 / (n_steps * 2)
+        byts = 6.0 * w4.f * w4.d + 2.0 * 16 * w4.d + 4.0 * 16 * w4.d
+        out["llama3_70b_chunk16"] = {"d": w4.d, "f": w4.f, "tokens": 16, "us_per_call": us,
+                                     "algorithmic_bytes_per_call": byts, "gbs": byts / (us * 1e-6) / 1e9,
+                                     "tflops": 2.0 * 3 * w4.f * w4.d * 16 / (us * 1e-6) / 1e12,
+                                     "ms_per_chunk_8_layers": 8 * us / 1e3}
+        log(f"  extra chunk16: {us:.1f} us/layer, {out['llama3_70b_chunk16']['gbs']:.0f} GB/s")
+        del layers, ws, X, Y
+        torch.cuda.empty_cache()
 
-    def chunk(tok, l):
-        return (lib.ffn_dense_chunk, (ctypes.byref(layers[l].c), X[tok, l].data_ptr(), 16, Y[l].data_ptr(), wsp, wsb))
-    time_mixed(torch, [[chunk(tok, l) for l in range(2)] for tok in range(n_warm)], mode)
-    ms = time_mixed(torch, [[chunk(tok, l) for l in range(2)] for tok in range(n_warm, n_warm + n_steps)], mode)
-    us = ms * 1e3 / (n_steps * 2)
-    byts = 6.0 * w4.f * w4.d + 2.0 * 16 * w4.d + 4.0 * 16 * w4.d
-    out["llama3_70b_chunk16"] = {"d": w4.d, "f": w4.f, "tokens": 16, "us_per_call": us,
-                                 "algorithmic_bytes_per_call": byts, "gbs": byts / (us * 1e-6) / 1e9,
-                                 "tflops": 2.0 * 3 * w4.f * w4.d * 16 / (us * 1e-6) / 1e12,
-                                 "ms_per_chunk_8_layers": 8 * us / 1e3}
-    log(f"  extra chunk16: {us:.1f} us/layer, {out['llama3_70b_chunk16']['gbs']:.0f} GB/s")
-    del layers, ws, X, Y
-    torch.cuda.empty_cache()
 
-    # Sirius correction period at the Llama-3-70B shape over an 8-layer group: 16 sparse
-    # CATS steps (each token through the 8 layers), then the dense verification of the
-    # same 16 tokens per layer, captured together and replayed; against full-model
-    # decoding (16 one-token dense calls per layer)
-    P, nlg = 16, w4.layers
-    layers = swiglu_layers(w4, w4.d, w4.f, nlg)
-    ws = B.workspace(max(B.sparse_ffn_workspace_size(layers[0], w4.n_cal), B.sparse_ffn_workspace_size(layers[0], P)))
-    t = calibrate(layers, w4, 0.5, ws)
-    n_per = 4  # one warm-up period, three timed
-    X = xtok(w4, (n_per, nlg, P, w4.d), inputs.STREAM_DECODE)
-    Ys = torch.zeros((nlg, P, w4.d), dtype=torch.float32, device=dev)
-    Yd = torch.zeros((nlg, P, w4.d), dtype=torch.float32, device=dev)
-    nact = torch.zeros((nlg, P), dtype=torch.int32, device=dev)
-    wsp, wsb = ws.data_ptr(), ws.numel()
+    def sirius_leg(w4):
+        # Sirius correction period at the Llama-3-70B shape over an 8-layer group: 16 sparse
+        # CATS steps (each token through the 8 layers), then the dense verification of the
+        # same 16 tokens per layer, captured together and replayed; against full-model
+        # decoding (16 one-token dense calls per layer)
+        P, nlg = 16, w4.layers
+        layers = swiglu_layers(w4, w4.d, w4.f, nlg)
+        ws = B.workspace(max(B.sparse_ffn_workspace_size(layers[0], w4.n_cal), B.sparse_ffn_workspace_size(layers[0], P)))
+        t = calibrate(layers, w4, 0.5, ws)
+        n_per = 4  # one warm-up period, three timed
+        X = xtok(w4, (n_per, nlg, P, w4.d), inputs.STREAM_DECODE)
+        Ys = torch.zeros((nlg, P, w4.d), dtype=torch.float32, device=dev)
+        Yd = torch.zeros((nlg, P, w4.d), dtype=torch.float32, device=dev)
+        nact = torch.zeros((nlg, P), dtype=torch.int32, device=dev)
+        wsp, wsb = ws.data_ptr(), ws.numel()
 
-    def sparse_step(per, j, counts=False):
-        return [(lib.sparse_ffn_decode, (ctypes.byref(layers[l].c), X[per, l, j].data_ptr(), 1, t[l:l + 1].data_ptr(),
-                                         None, None, None, Ys[l, j].data_ptr(), None,
-                                         nact[l, j:j + 1].data_ptr() if counts else None, wsp, wsb))
-                for l in range(nlg)]
+        def sparse_step(per, j, counts=False):
+            return [(lib.sparse_ffn_decode, (ctypes.byref(layers[l].c), X[per, l, j].data_ptr(), 1, t[l:l + 1].data_ptr(),
+                                             None, None, None, Ys[l, j].data_ptr(), None,
+                                             nact[l, j:j + 1].data_ptr() if counts else None, wsp, wsb))
+                    for l in range(nlg)]
 
-    def verify(per):
-        return [(lib.ffn_dense_chunk, (ctypes.byref(layers[l].c), X[per, l].data_ptr(), P, Yd[l].data_ptr(), wsp, wsb))
-                for l in range(nlg)]
+        def verify(per):
+            return [(lib.ffn_dense_chunk, (ctypes.byref(layers[l].c), X[per, l].data_ptr(), P, Yd[l].data_ptr(), wsp, wsb))
+                    for l in range(nlg)]
 
-    def dense_tokens(per):
-        return [(lib.ffn_dense_chunk, (ctypes.byref(layers[l].c), X[per, l, j].data_ptr(), 1, Ys[l, j].data_ptr(),
-                                       wsp, wsb)) for j in range(P) for l in range(nlg)]
+        def dense_tokens(per):
+            return [(lib.ffn_dense_chunk, (ctypes.byref(layers[l].c), X[per, l, j].data_ptr(), 1, Ys[l, j].data_ptr(),
+                                           wsp, wsb)) for j in range(P) for l in range(nlg)]
 
-    def period(per, counts=False):
-        return [c for j in range(P) for c in sparse_step(per, j, counts)] + verify(per)
-    time_mixed(torch, [period(0)], mode)
-    per_ms = time_mixed(torch, [period(p) for p in range(1, n_per)], mode) / (n_per - 1)
-    sparse_ms = time_mixed(torch, [[c for j in range(P) for c in sparse_step(p, j)] for p in range(1, n_per)],
-                           mode) / (n_per - 1)
-    verify_ms = time_mixed(torch, [verify(p) for p in range(1, n_per)], mode) / (n_per - 1)
-    time_mixed(torch, [dense_tokens(0)], mode)
-    dense_ms = time_mixed(torch, [dense_tokens(p) for p in range(1, n_per)], mode) / (n_per - 1)
-    # outputs and active counts of the last period (untimed), then the statistics
-    for fn, a in period(n_per - 1, counts=True):
-        fn(*a, torch.cuda.current_stream().cuda_stream)
-    torch.cuda.synchronize()
-    div = ((Ys - Yd).norm(dim=-1) / Yd.norm(dim=-1)).flatten().cpu().numpy()
-    dens = float(nact.float().mean().item()) / w4.f
-    rho = (1.0 + 2.0 * dens) / 3.0  # a CATS step's weight bytes over a dense token's
-    dense_tok_bytes = 6.0 * w4.f * w4.d * nlg
-    res = {"d": w4.d, "f": w4.f, "layers": nlg, "period": P, "sparsity": 0.5, "active_density": dens,
-           "period_ms": per_ms, "sparse_steps_ms": sparse_ms, "verify_ms": verify_ms,
-           "dense_decode_16_tokens_ms": dense_ms,
-           "divergence": {"mean": float(div.mean()), "p90": float(np.quantile(div, 0.9)), "max": float(div.max())}}
-    # accepted advance length: all 16, and 15.37 of 16 (the page's GSM8K figure)
-    for name, aal in (("aal16", 16.0), ("aal15.37", 15.37)):
-        res[name] = {"tokens_per_s": aal / (per_ms * 1e-3), "latency_vs_full": (per_ms / aal) / (dense_ms / P),
-                     "effective_density": (P * rho + 1.0) / aal,
-                     "effective_bytes_per_token": (P * rho + 1.0) * dense_tok_bytes / aal}
-    out["llama3_70b_sirius_period16"] = res
-    log(f"  extra sirius period: {per_ms:.3f} ms ({sparse_ms:.3f} sparse + {verify_ms:.3f} verify), dense 16 tokens "
-        f"{dense_ms:.3f} ms, latency vs full {res['aal16']['latency_vs_full']:.3f}, divergence mean "
-        f"{res['divergence']['mean']:.4f}")
-    del layers, ws, X, Ys, Yd
-    torch.cuda.empty_cache()
-
-    # ReGLU layers with SVD predictors (factors and thresholds from the offline
-    # preparation): the sequential pipeline with a rank-256 predictor (predict, then the
-    # gate on the candidates and up/down where ReLU(gate) > 0) and the parallel pipeline
-    # with a rank-1024 whitened predictor (predict, then gate, up and down rows of every
-    # candidate in one pass)
-    from contextual_activation_sparsity_amd import prepare
-    w3 = inputs.workload(3)
-    d, f = w3.d, w3.f
-    layers, pred_seq, pred_par = [], [], []
-    # calibration tokens for whitening and thresholds: 2d of them (whitening needs n >= d)
-    xcal = xtok(w3, (max(w3.n_tau_cal, 2 * d), d), inputs.STREAM_TAU)
-    t0 = time.perf_counter()
-    for l in range(n_layers):
-        A = torch.randn((f, w3.rank), generator=torch.Generator(device=dev).manual_seed(
-            inputs.seed(3, l, inputs.T_A)), device=dev) / np.sqrt(w3.rank)
-        Bm = torch.randn((w3.rank, d), generator=torch.Generator(device=dev).manual_seed(
-            inputs.seed(3, l, inputs.T_B)), device=dev) * w3.w_std
-        noise = torch.randn((f, d), generator=torch.Generator(device=dev).manual_seed(
-            inputs.seed(3, l, inputs.T_NOISE)), device=dev) * w3.w_std
-        wg = (A @ Bm + 0.1 * noise).to(torch.bfloat16)
-        del A, Bm, noise
-        bias = (-1.2815516 * wg.float().norm(dim=1)).contiguous()
-        gates = xcal.float() @ wg.float().t() + bias
-        for preds, r, whiten in ((pred_seq, 256, False), (pred_par, 1024, True)):
-            q, lf = prepare.svd_factors(wg, r, x_cal=xcal if whiten else None)
-            tau = prepare.calibrate_tau(prepare.predictions(q, lf, xcal.float(), bias), gates, w3.s)
-            preds.append(B.SVDPredictor(q, lf, tau, b=bias))
-            torch.cuda.synchronize()
-            log(f"  layer {l}: rank-{r} {'whitened ' if whiten else ''}factors and thresholds at "
-                f"{time.perf_counter() - t0:.1f} s")
-        del gates
-        layers.append(B.FFNLayer(wg, gauss((f, d), w3.w_std, inputs.seed(3, l, inputs.T_UP)),
-                                 gauss((f, d), w3.w_std, inputs.seed(3, l, inputs.T_DOWN)), b_gate=bias,
-                                 act=B.SFN_ACT_RELU))
-    torch.cuda.synchronize()
-    log(f"  svd factors and thresholds for {n_layers} layers in {time.perf_counter() - t0:.1f} s")
-    ws = B.workspace(B.sparse_ffn_workspace_size(layers[0], 1))
-    wsp_ = B.workspace(max(B.svd_predict_workspace_size(pred_seq[0]), B.svd_predict_workspace_size(pred_par[0])))
-    X = xtok(w3, (n_warm + n_steps, n_layers, d), inputs.STREAM_DECODE)
-    y = torch.zeros((n_layers, d), dtype=torch.float32, device=dev)
-    cand = torch.zeros((n_layers, f), dtype=torch.int32, device=dev)
-    ncand = torch.zeros((n_layers, 1), dtype=torch.int32, device=dev)
-    nact = torch.zeros((n_layers, 1), dtype=torch.int32, device=dev)
-
-    def predict(preds, tok, l):
-        return (lib.svd_predict, (ctypes.byref(preds[l].c), X[tok, l].data_ptr(), cand[l].data_ptr(),
-                                  ncand[l].data_ptr(), None, wsp_.data_ptr(), wsp_.numel()))
-
-    def seq_calls(tok, l, counts=False):
-        return [predict(pred_seq, tok, l),
-                (lib.sparse_ffn_decode, (ctypes.byref(layers[l].c), X[tok, l].data_ptr(), 1, None,
-                                         cand[l].data_ptr(), ncand[l].data_ptr(), None, y[l].data_ptr(), None,
-                                         nact[l].data_ptr() if counts else None, ws.data_ptr(), ws.numel()))]
-
-    def par_calls(tok, l):
-        return [predict(pred_par, tok, l),
-                (lib.sparse_ffn_decode_parallel, (ctypes.byref(layers[l].c), X[tok, l].data_ptr(), cand[l].data_ptr(),
-                                                  ncand[l].data_ptr(), y[l].data_ptr(), ws.data_ptr(), ws.numel()))]
-
-    def leg(calls):
-        steps = [[c for l in range(n_layers) for c in calls(tok, l)] for tok in range(n_warm, n_warm + n_steps)]
-        time_mixed(torch, [[c for l in range(n_layers) for c in calls(tok, l)] for tok in range(n_warm)], mode)
-        return time_mixed(torch, steps, mode) * 1e3 / (n_steps * n_layers)
-
-    # densities: untimed passes over the timed tokens
-    dc, da, dcp = [], [], []
-    for tok in range(n_warm, n_warm + n_steps):
-        for l in range(n_layers):
-            for fn, a in seq_calls(tok, l, True):
-                fn(*a, torch.cuda.current_stream().cuda_stream)
-        torch.cuda.synchronize()
-        dc.append(ncand.float().mean().item())
-        da.append(nact.float().mean().item())
-        for l in range(n_layers):
-            fn, a = predict(pred_par, tok, l)
+        def period(per, counts=False):
+            return [c for j in range(P) for c in sparse_step(per, j, counts)] + verify(per)
+        time_mixed(torch, [period(0)], mode)
+        per_ms = time_mixed(torch, [period(p) for p in range(1, n_per)], mode) / (n_per - 1)
+        sparse_ms = time_mixed(torch, [[c for j in range(P) for c in sparse_step(p, j)] for p in range(1, n_per)],
+                               mode) / (n_per - 1)
+        verify_ms = time_mixed(torch, [verify(p) for p in range(1, n_per)], mode) / (n_per - 1)
+        time_mixed(torch, [dense_tokens(0)], mode)
+        dense_ms = time_mixed(torch, [dense_tokens(p) for p in range(1, n_per)], mode) / (n_per - 1)
+        # outputs and active counts of the last period (untimed), then the statistics
+        for fn, a in period(n_per - 1, counts=True):
             fn(*a, torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
-        dcp.append(ncand.float().mean().item())
-    nc, na, ncp = float(np.mean(dc)), float(np.mean(da)), float(np.mean(dcp))
-    for name, r, calls, byts in (
-            ("reglu_svd_r256_s50", 256, seq_calls, 2.0 * 256 * (d + f) + 8.0 * f + 2.0 * nc * d + 4.0 * na * d + 6.0 * d),
-            ("reglu_svd_r1024_whitened_parallel", 1024, par_calls,
-             2.0 * 1024 * (d + f) + 8.0 * f + 6.0 * ncp * d + 6.0 * d)):
-        us = leg(calls)
-        preds = pred_seq if r == 256 else pred_par
-        pred_us = time_mixed(torch, [[predict(preds, tok, l) for l in range(n_layers)]
-                                     for tok in range(n_warm, n_warm + n_steps)], mode) * 1e3 / (n_steps * n_layers)
-        out[name] = {"d": d, "f": f, "r": r, "s": w3.s, "layers_timed": n_layers, "us_per_layer": us,
-                     "predictor_us": pred_us, "candidate_density": (nc if r == 256 else ncp) / f,
-                     "algorithmic_bytes_per_layer": byts, "gbs": byts / (us * 1e-6) / 1e9,
-                     "tokens_per_s_32_layers": 1.0 / (32 * us * 1e-6)}
-        if r == 256:
-            out[name]["active_density"] = na / f
-        log(f"  extra {name}: {us:.2f} us/layer (predictor {pred_us:.2f}), cand {out[name]['candidate_density']:.3f}")
+        div = ((Ys - Yd).norm(dim=-1) / Yd.norm(dim=-1)).flatten().cpu().numpy()
+        dens = float(nact.float().mean().item()) / w4.f
+        rho = (1.0 + 2.0 * dens) / 3.0  # a CATS step's weight bytes over a dense token's
+        dense_tok_bytes = 6.0 * w4.f * w4.d * nlg
+        res = {"d": w4.d, "f": w4.f, "layers": nlg, "period": P, "sparsity": 0.5, "active_density": dens,
+               "period_ms": per_ms, "sparse_steps_ms": sparse_ms, "verify_ms": verify_ms,
+               "dense_decode_16_tokens_ms": dense_ms,
+               "divergence": {"mean": float(div.mean()), "p90": float(np.quantile(div, 0.9)), "max": float(div.max())}}
+        # accepted advance length: all 16, and 15.37 of 16 (the page's GSM8K figure)
+        for name, aal in (("aal16", 16.0), ("aal15.37", 15.37)):
+            res[name] = {"tokens_per_s": aal / (per_ms * 1e-3), "latency_vs_full": (per_ms / aal) / (dense_ms / P),
+                         "effective_density": (P * rho + 1.0) / aal,
+                         "effective_bytes_per_token": (P * rho + 1.0) * dense_tok_bytes / aal}
+        out["llama3_70b_sirius_period16"] = res
+        log(f"  extra sirius period: {per_ms:.3f} ms ({sparse_ms:.3f} sparse + {verify_ms:.3f} verify), dense 16 tokens "
+            f"{dense_ms:.3f} ms, latency vs full {res['aal16']['latency_vs_full']:.3f}, divergence mean "
+            f"{res['divergence']['mean']:.4f}")
+        del layers, ws, X, Ys, Yd
+        torch.cuda.empty_cache()
 
-    # the same two pipelines through the fused call: each tile predicts its own rows and
-    # processes its candidates, no candidate list in between (same bytes)
-    wsf = B.workspace(max(B.sparse_ffn_svd_workspace_size(layers[0], pred_seq[0]),
-                          B.sparse_ffn_svd_workspace_size(layers[0], pred_par[0])))
 
-    def fused(preds, pipe):
-        return lambda tok, l: [(lib.sparse_ffn_decode_svd, (ctypes.byref(layers[l].c), ctypes.byref(preds[l].c),
-                                                            X[tok, l].data_ptr(), pipe, y[l].data_ptr(), None, None,
-                                                            wsf.data_ptr(), wsf.numel()))]
-    for name, base, calls in (("reglu_svd_r256_s50_fused", "reglu_svd_r256_s50", fused(pred_seq, B.SFN_PIPE_SEQUENTIAL)),
-                              ("reglu_svd_r1024_whitened_parallel_fused", "reglu_svd_r1024_whitened_parallel",
-                               fused(pred_par, B.SFN_PIPE_PARALLEL))):
-        us = leg(calls)
-        byts = out[base]["algorithmic_bytes_per_layer"]
-        out[name] = {"d": d, "f": f, "r": out[base]["r"], "s": w3.s, "layers_timed": n_layers, "us_per_layer": us,
-                     "algorithmic_bytes_per_layer": byts, "gbs": byts / (us * 1e-6) / 1e9,
-                     "tokens_per_s_32_layers": 1.0 / (32 * us * 1e-6), "speedup_over_unfused": out[base]["us_per_layer"] / us}
-        log(f"  extra {name}: {us:.2f} us/layer ({out[name]['gbs']:.0f} GB/s), "
-            f"{out[name]['speedup_over_unfused']:.2f}x the unfused calls")
+    def svd_legs():
+        # ReGLU layers with SVD predictors (factors and thresholds from the offline
+        # preparation): the sequential pipeline with a rank-256 predictor (predict, then the
+        # gate on the candidates and up/down where ReLU(gate) > 0) and the parallel pipeline
+        # with a rank-1024 whitened predictor (predict, then gate, up and down rows of every
+        # candidate in one pass)
+        from contextual_activation_sparsity_amd import prepare
+        w3 = inputs.workload(3)
+        d, f = w3.d, w3.f
+        layers, pred_seq, pred_par = [], [], []
+        # calibration tokens for whitening and thresholds: 2d of them (whitening needs n >= d)
+        xcal = xtok(w3, (max(w3.n_tau_cal, 2 * d), d), inputs.STREAM_TAU)
+        t0 = time.perf_counter()
+        for l in range(svd_prepared):
+            A = torch.randn((f, w3.rank), generator=torch.Generator(device=dev).manual_seed(
+                inputs.seed(3, l, inputs.T_A)), device=dev) / np.sqrt(w3.rank)
+            Bm = torch.randn((w3.rank, d), generator=torch.Generator(device=dev).manual_seed(
+                inputs.seed(3, l, inputs.T_B)), device=dev) * w3.w_std
+            noise = torch.randn((f, d), generator=torch.Generator(device=dev).manual_seed(
+                inputs.seed(3, l, inputs.T_NOISE)), device=dev) * w3.w_std
+            wg = (A @ Bm + 0.1 * noise).to(torch.bfloat16)
+            del A, Bm, noise
+            bias = (-1.2815516 * wg.float().norm(dim=1)).contiguous()
+            gates = xcal.float() @ wg.float().t() + bias
+            for preds, r, whiten in ((pred_seq, 256, False), (pred_par, 1024, True)):
+                q, lf = prepare.svd_factors(wg, r, x_cal=xcal if whiten else None)
+                tau = prepare.calibrate_tau(prepare.predictions(q, lf, xcal.float(), bias), gates, w3.s)
+                preds.append(B.SVDPredictor(q, lf, tau, b=bias))
+                torch.cuda.synchronize()
+                log(f"  layer {l}: rank-{r} {'whitened ' if whiten else ''}factors and thresholds at "
+                    f"{time.perf_counter() - t0:.1f} s")
+            del gates
+            layers.append(B.FFNLayer(wg, gauss((f, d), w3.w_std, inputs.seed(3, l, inputs.T_UP)),
+                                     gauss((f, d), w3.w_std, inputs.seed(3, l, inputs.T_DOWN)), b_gate=bias,
+                                     act=B.SFN_ACT_RELU))
+        torch.cuda.synchronize()
+        log(f"  svd factors and thresholds for {svd_prepared} layers in {time.perf_counter() - t0:.1f} s")
+        # the timed stack: svd_layers layers, layer l a copy of prepared layer l % svd_prepared
+        # in memory of its own, so the working set (about 10 GB of weights and factors over
+        # 32 layers) is streamed from HBM on every token, as 32 distinct layers would be;
+        # preparing each layer separately would add seconds of SVD per layer and change
+        # neither the bytes nor the densities
+        def copy_layer(src):
+            return B.FFNLayer(src.w_gate.clone(), src.w_up.clone(), src.w_down_t.clone(), b_gate=src.b_gate.clone(),
+                              act=src.act)
+
+        def copy_pred(src):
+            return B.SVDPredictor(src.q.clone(), src.l.clone(), src.tau.clone(), b=src.b.clone())
+        n_layers = svd_layers
+        layers = [layers[l] if l < svd_prepared else copy_layer(layers[l % svd_prepared]) for l in range(n_layers)]
+        pred_seq = [pred_seq[l] if l < svd_prepared else copy_pred(pred_seq[l % svd_prepared]) for l in range(n_layers)]
+        pred_par = [pred_par[l] if l < svd_prepared else copy_pred(pred_par[l % svd_prepared]) for l in range(n_layers)]
+        torch.cuda.synchronize()
+        ws = B.workspace(B.sparse_ffn_workspace_size(layers[0], 1))
+        wsp_ = B.workspace(max(B.svd_predict_workspace_size(pred_seq[0]), B.svd_predict_workspace_size(pred_par[0])))
+        X = xtok(w3, (n_warm + n_steps, n_layers, d), inputs.STREAM_DECODE)
+        y = torch.zeros((n_layers, d), dtype=torch.float32, device=dev)
+        cand = torch.zeros((n_layers, f), dtype=torch.int32, device=dev)
+        ncand = torch.zeros((n_layers, 1), dtype=torch.int32, device=dev)
+        nact = torch.zeros((n_layers, 1), dtype=torch.int32, device=dev)
+
+        def predict(preds, tok, l):
+            return (lib.svd_predict, (ctypes.byref(preds[l].c), X[tok, l].data_ptr(), cand[l].data_ptr(),
+                                      ncand[l].data_ptr(), None, wsp_.data_ptr(), wsp_.numel()))
+
+        def seq_calls(tok, l, counts=False):
+            return [predict(pred_seq, tok, l),
+                    (lib.sparse_ffn_decode, (ctypes.byref(layers[l].c), X[tok, l].data_ptr(), 1, None,
+                                             cand[l].data_ptr(), ncand[l].data_ptr(), None, y[l].data_ptr(), None,
+                                             nact[l].data_ptr() if counts else None, ws.data_ptr(), ws.numel()))]
+
+        def par_calls(tok, l):
+            return [predict(pred_par, tok, l),
+                    (lib.sparse_ffn_decode_parallel, (ctypes.byref(layers[l].c), X[tok, l].data_ptr(), cand[l].data_ptr(),
+                                                      ncand[l].data_ptr(), y[l].data_ptr(), ws.data_ptr(), ws.numel()))]
+
+        def leg(calls):
+            steps = [[c for l in range(n_layers) for c in calls(tok, l)] for tok in range(n_warm, n_warm + n_steps)]
+            time_mixed(torch, [[c for l in range(n_layers) for c in calls(tok, l)] for tok in range(n_warm)], mode)
+            return time_mixed(torch, steps, mode) * 1e3 / (n_steps * n_layers)
+
+        # densities: untimed passes over the timed tokens
+        dc, da, dcp = [], [], []
+        for tok in range(n_warm, n_warm + n_steps):
+            for l in range(n_layers):
+                for fn, a in seq_calls(tok, l, True):
+                    fn(*a, torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            dc.append(ncand.float().mean().item())
+            da.append(nact.float().mean().item())
+            for l in range(n_layers):
+                fn, a = predict(pred_par, tok, l)
+                fn(*a, torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            dcp.append(ncand.float().mean().item())
+        nc, na, ncp = float(np.mean(dc)), float(np.mean(da)), float(np.mean(dcp))
+        for name, r, calls, byts in (
+                ("reglu_svd_r256_s50", 256, seq_calls, 2.0 * 256 * (d + f) + 8.0 * f + 2.0 * nc * d + 4.0 * na * d + 6.0 * d),
+                ("reglu_svd_r1024_whitened_parallel", 1024, par_calls,
+                 2.0 * 1024 * (d + f) + 8.0 * f + 6.0 * ncp * d + 6.0 * d)):
+            us = leg(calls)
+            preds = pred_seq if r == 256 else pred_par
+            pred_us = time_mixed(torch, [[predict(preds, tok, l) for l in range(n_layers)]
+                                         for tok in range(n_warm, n_warm + n_steps)], mode) * 1e3 / (n_steps * n_layers)
+            out[name] = {"d": d, "f": f, "r": r, "s": w3.s, "layers_timed": n_layers,
+                         "distinct_layer_values": svd_prepared, "us_per_layer": us,
+                         "predictor_us": pred_us, "candidate_density": (nc if r == 256 else ncp) / f,
+                         "algorithmic_bytes_per_layer": byts, "gbs": byts / (us * 1e-6) / 1e9,
+                         "tokens_per_s": 1.0 / (n_layers * us * 1e-6)}
+            if r == 256:
+                out[name]["active_density"] = na / f
+            log(f"  extra {name}: {us:.2f} us/layer (predictor {pred_us:.2f}), cand {out[name]['candidate_density']:.3f}")
+
+        # the same two pipelines through the fused call: each tile predicts its own rows and
+        # processes its candidates, no candidate list in between (same bytes)
+        wsf = B.workspace(max(B.sparse_ffn_svd_workspace_size(layers[0], pred_seq[0]),
+                              B.sparse_ffn_svd_workspace_size(layers[0], pred_par[0])))
+
+        def fused(preds, pipe):
+            return lambda tok, l: [(lib.sparse_ffn_decode_svd, (ctypes.byref(layers[l].c), ctypes.byref(preds[l].c),
+                                                                X[tok, l].data_ptr(), pipe, y[l].data_ptr(), None, None,
+                                                                wsf.data_ptr(), wsf.numel()))]
+        for name, base, calls in (("reglu_svd_r256_s50_fused", "reglu_svd_r256_s50", fused(pred_seq, B.SFN_PIPE_SEQUENTIAL)),
+                                  ("reglu_svd_r1024_whitened_parallel_fused", "reglu_svd_r1024_whitened_parallel",
+                                   fused(pred_par, B.SFN_PIPE_PARALLEL))):
+            us = leg(calls)
+            byts = out[base]["algorithmic_bytes_per_layer"]
+            out[name] = {"d": d, "f": f, "r": out[base]["r"], "s": w3.s, "layers_timed": n_layers,
+                         "distinct_layer_values": svd_prepared, "us_per_layer": us,
+                         "algorithmic_bytes_per_layer": byts, "gbs": byts / (us * 1e-6) / 1e9,
+                         "tokens_per_s": 1.0 / (n_layers * us * 1e-6),
+                         "speedup_over_unfused": out[base]["us_per_layer"] / us}
+            log(f"  extra {name}: {us:.2f} us/layer ({out[name]['gbs']:.0f} GB/s), "
+                f"{out[name]['speedup_over_unfused']:.2f}x the unfused calls")
+
+    if "tiny" in legs:
+        # the tiny fp32 SwiGLU layer (d 256, f 688; 2.1 MB of weights, resident in the
+        # caches): latency per call, all 64 decode tokens, threshold from 256 calibration
+        # tokens; a graph of one call per token replayed back to back
+        w0 = inputs.workload(0)
+        l0 = [B.FFNLayer(*(torch.from_numpy(inputs.swiglu_layer(w0, 0)[k]).to(dev)
+                           for k in ("w_gate", "w_up", "w_down_t")))]
+        ws0 = B.workspace(B.sparse_ffn_workspace_size(l0[0], w0.n_cal))
+        xc0 = torch.from_numpy(inputs.tokens(w0, w0.n_cal, inputs.STREAM_CAL)).to(dev)
+        t0v = torch.zeros(1, dtype=torch.float32, device=dev)
+        B.sparse_ffn_calibrate(l0[0], xc0, 0.5, t0v, ws0)
+        X0 = torch.from_numpy(inputs.tokens(w0, w0.decode_tokens, inputs.STREAM_DECODE)).to(dev)
+        y0 = torch.zeros((w0.decode_tokens, w0.d), dtype=torch.float32, device=dev)
+        n0 = torch.zeros(w0.decode_tokens, dtype=torch.int32, device=dev)
+
+        def tiny(tok, counts=False):
+            return (lib.sparse_ffn_decode, (ctypes.byref(l0[0].c), X0[tok].data_ptr(), 1, t0v.data_ptr(), None, None,
+                                            None, y0[tok].data_ptr(), None,
+                                            n0[tok:tok + 1].data_ptr() if counts else None, ws0.data_ptr(),
+                                            ws0.numel()))
+        for tok in range(w0.decode_tokens):
+            fn, a = tiny(tok, True)
+            fn(*a, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        ntok = w0.decode_tokens
+        # back to back: the 64 calls in one graph (per-call time in a stream of calls);
+        # isolated: one graph per call, so each also pays the graph launch
+        time_mixed(torch, [[tiny(tok) for tok in range(ntok)]], mode)
+        ms = time_mixed(torch, [[tiny(tok) for tok in range(ntok)]], mode)
+        ms_iso = time_mixed(torch, [[tiny(tok)] for tok in range(ntok)], mode)
+        out["tiny_fp32_d256_f688_k50"] = {"d": w0.d, "f": w0.f, "dtype": "f32", "tokens": ntok,
+                                          "us_per_call": ms * 1e3 / ntok,
+                                          "us_per_call_isolated": ms_iso * 1e3 / ntok,
+                                          "measured_density": float(n0.float().mean().item()) / w0.f,
+                                          "note": "2.1 MB of weights stay in the caches: latency only"}
+        log(f"  extra tiny fp32 layer: {ms * 1e3 / ntok:.2f} us per call back to back, "
+            f"{ms_iso * 1e3 / ntok:.2f} us isolated")
+        del l0, ws0, xc0, X0, y0
+
+    # batch of 4 with per-token masks and the union gather (Llama-3-8B shape), and batch 1
+    w2 = inputs.workload(2)
+    if "b4" in legs:
+        decode_leg("llama3_8b_b4_k50", w2, w2.d, w2.f, 4, 0.5, n_layers)
+        decode_leg("llama3_8b_b4_k60", w2, w2.d, w2.f, 4, 0.6, n_layers)
+    if "b1" in legs:
+        decode_leg("llama3_8b_b1_k50", w2, w2.d, w2.f, 1, 0.5, n_layers)
+        decode_leg("llama3_8b_b1_k60", w2, w2.d, w2.f, 1, 0.6, n_layers)
+    # sparse decode at the Llama-3-70B shape (d 8192: two 16-byte chunks per thread)
+    w4 = inputs.workload(4)
+    if "70b" in legs:
+        decode_leg("llama3_70b_b1_k50", w4, w4.d, w4.f, 1, 0.5, 2)
+    if "chunk" in legs:
+        chunk_leg(w4)
+    if "sirius" in legs:
+        sirius_leg(w4)
+    if "svd" in legs:
+        svd_legs()
     return out
+
 
 
 def cpu_baseline(stack, k, budget_s):
@@ -731,7 +811,11 @@ def main():
     extra = None
     if not args.no_extras:
         log("timing the other workloads")
-        extra = extras(B, inputs, torch, args.mode)
+        legs = tuple(x.strip() for x in args.legs.split(",") if x.strip())
+        unknown = set(legs) - set(EXTRA_LEGS)
+        if unknown:
+            raise SystemExit(f"unknown --legs entries: {sorted(unknown)}")
+        extra = extras(B, inputs, torch, args.mode, legs=legs)
 
     t4 = None
     if not args.no_table4:
