@@ -78,16 +78,26 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other workloads (batch 4, SVD pipeline, 70B-shape decode and 16-token chunk)")
+    ap.add_argument("--svd-layers", type=int, default=32, help="layers of the timed SVD stacks")
+    ap.add_argument("--svd-prepared", type=int, default=4,
+                    help="distinct prepared ReGLU layers (factors, thresholds) the SVD stacks copy")
+    ap.add_argument("--svd-prep-host", action="store_true",
+                    help="compute the SVD legs' factors on the host in float64 instead of on the device")
     ap.add_argument("--legs", default=",".join(EXTRA_LEGS),
                     help="comma list of the other workloads to run: " + ", ".join(EXTRA_LEGS))
     ap.add_argument("--no-table4", action="store_true",
                     help="skip the fixed-sparsity protocol (random candidate subsets on every layer, three shapes)")
+    ap.add_argument("--t4-shapes", default="0,1,2",
+                    help="comma list of the fixed-sparsity protocol's shapes to run (0: 4096/11008, 1: 4096/14336, "
+                         "2: 3584/18944)")
+    ap.add_argument("--t4-sparsities", default="0.2,0.5,0.8,0.95")
     ap.add_argument("--no-quality", action="store_true",
                     help="skip the predictor-quality diagnostics (ROC AUC and recall against rank and s)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before the stack, copy a MIB-MiB buffer three times (counter scaling)")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-kernel-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--command", default="", help="profiling command recorded in a summary")
     return ap.parse_args()
 
@@ -301,7 +311,7 @@ EXTRA_LEGS = ("tiny", "b4", "b1", "70b", "chunk", "sirius", "svd")
 
 
 def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4, legs=EXTRA_LEGS, svd_layers=32,
-           svd_prepared=4):
+           svd_prepared=4, svd_prep_host=False):
     """The other workloads, each timed like the headline (graphs of per-layer calls, HIP
     events over the timed steps) on n_layers independently seeded layers: per-call time,
     algorithmic bytes and GB/s. Inputs as in the headline: on-device Gaussian weights,
@@ -484,7 +494,10 @@ def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4, legs=EXTRA_
             bias = (-1.2815516 * wg.float().norm(dim=1)).contiguous()
             gates = xcal.float() @ wg.float().t() + bias
             for preds, r, whiten in ((pred_seq, 256, False), (pred_par, 1024, True)):
-                q, lf = prepare.svd_factors(wg, r, x_cal=xcal if whiten else None)
+                if svd_prep_host:  # float64 on the host (the device SVD is the other route)
+                    q, lf = (t.to(dev) for t in prepare.svd_factors(wg.cpu(), r, x_cal=xcal.cpu() if whiten else None))
+                else:
+                    q, lf = prepare.svd_factors(wg, r, x_cal=xcal if whiten else None)
                 tau = prepare.calibrate_tau(prepare.predictions(q, lf, xcal.float(), bias), gates, w3.s)
                 preds.append(B.SVDPredictor(q, lf, tau, b=bias))
                 torch.cuda.synchronize()
@@ -708,6 +721,8 @@ def main():
         return 0
     if args.summarize_traffic:
         return write_traffic(args.summarize_traffic, args.copy_probe << 20, args.command)
+    if args.summarize_kernel_traffic:
+        return summarize_kernel_traffic(*args.summarize_kernel_traffic, args.copy_probe << 20, args.command)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this library has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Run with --gpus 1.", file=sys.stderr)
@@ -815,12 +830,14 @@ def main():
         unknown = set(legs) - set(EXTRA_LEGS)
         if unknown:
             raise SystemExit(f"unknown --legs entries: {sorted(unknown)}")
-        extra = extras(B, inputs, torch, args.mode, legs=legs)
+        extra = extras(B, inputs, torch, args.mode, legs=legs, svd_layers=args.svd_layers,
+                       svd_prepared=min(args.svd_prepared, args.svd_layers), svd_prep_host=args.svd_prep_host)
 
     t4 = None
     if not args.no_table4:
         log("fixed-sparsity protocol (predictor excluded)")
-        t4 = table4(B, inputs, torch, args.mode)
+        t4 = table4(B, inputs, torch, args.mode, shapes=tuple(T4_SHAPES[int(i)] for i in args.t4_shapes.split(",") if i),
+                    sparsities=tuple(float(v) for v in args.t4_sparsities.split(",") if v))
 
     quality = None
     if not args.no_quality:
@@ -853,8 +870,11 @@ def main():
     return 0
 
 
-def table4(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4,
-           shapes=((1, 4096, 11008), (2, 4096, 14336), (5, 3584, 18944)), sparsities=(0.2, 0.5, 0.8, 0.95)):
+T4_SHAPES = ((1, 4096, 11008), (2, 4096, 14336), (5, 3584, 18944))  # (workload, d, f)
+
+
+def table4(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4, shapes=T4_SHAPES,
+           sparsities=(0.2, 0.5, 0.8, 0.95)):
     """The fixed-sparsity protocol of "SVD Contextual Sparsity Predictors for Fast LLM
     Inference", Table 4: the same sparsity on every layer and on every projection, the
     gate included, predictor excluded. Each token and layer gets its own uniformly drawn
@@ -996,6 +1016,68 @@ def predictor_quality(B, inputs, torch, ranks=(16, 32, 64, 128, 256, 512, 1024),
                 f"candidates {t['candidate_density']:.3f}")
         out["tokens"][tname] = res
     return out
+
+
+def summarize_kernel_traffic(fetch_dir, write_dir, probe, command):
+    """Markdown table of HBM bytes per dispatch of each of the library's kernels, from a
+    FETCH_SIZE and a WRITE_SIZE --pmc run of the same command with the copy probe, each
+    counter scaled so that the probe's copy of `probe` bytes reads (writes) exactly `probe`
+    bytes. A kernel instance that serves several workloads (one grid, different row
+    counts) reads different amounts per dispatch: its dispatches are split into clusters
+    of bytes read (a new cluster wherever the sorted values jump by more than 5%), and each
+    cluster gets a line with its median read and the median write of the same dispatches
+    (the two runs dispatch in the same order, so the n-th dispatch of an instance is the
+    same call in both)."""
+    import statistics
+    if probe <= 0:
+        raise SystemExit("--copy-probe MIB must give the probe's size")
+    vals, scale = {}, {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per, copies = {}, []
+        rows = sorted((r for r in _csv_rows(d, "counter_collection.csv") if r.get("Counter_Name") == counter),
+                      key=lambda r: int(r["Dispatch_Id"]))
+        for r in rows:
+            name = r["Kernel_Name"]
+            v = float(r["Counter_Value"]) * 1024.0
+            if _short(name) == COPY_KERNEL:
+                copies.append(v)
+                continue
+            if "sfn::" not in name:
+                continue
+            wgs = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+            per.setdefault((_short(name, keep_args=True), wgs, int(r["Workgroup_Size"])), []).append(v)
+        if not copies:
+            raise SystemExit(f"{counter}: the copy probe's kernel is missing")
+        scale[counter] = probe / statistics.median(copies)
+        vals[counter] = {k: [x * scale[counter] for x in v] for k, v in per.items()}
+    out = ["# rocprofv3 HBM traffic per dispatch", "", "Commands:", "", "```", command or "(not recorded)", "```", "",
+           f"FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of each kernel, scaled by what the counters read for a "
+           f"plain elementwise copy (torch.neg) of {probe >> 20} MiB in the same run: FETCH x "
+           f"{scale['FETCH_SIZE']:.4f}, WRITE x {scale['WRITE_SIZE']:.4f}. One line per cluster of dispatches that "
+           f"read about the same bytes (an instance serving several workloads has several).", "",
+           "| kernel | workgroups x threads | dispatches | read MB (median) | read MB (min-max) | written MB (median) |",
+           "|---|---|---|---|---|---|"]
+    lines = []
+    for key, fv in vals["FETCH_SIZE"].items():
+        wv = vals["WRITE_SIZE"].get(key, [])
+        paired = len(wv) == len(fv)
+        order = sorted(range(len(fv)), key=lambda i: fv[i])
+        clusters, cur = [], [order[0]]
+        for a, b in zip(order, order[1:]):
+            if fv[b] > 1.05 * fv[a] + 1e3:
+                clusters.append(cur)
+                cur = []
+            cur.append(b)
+        clusters.append(cur)
+        for c in clusters:
+            rd = [fv[i] for i in c]
+            wr = statistics.median([wv[i] for i in c]) / 1e6 if paired else float("nan")
+            lines.append((statistics.median(rd), f"| `{key[0]}` | {key[1]} x {key[2]} | {len(c)} | "
+                                                 f"{statistics.median(rd) / 1e6:.2f} | {min(rd) / 1e6:.2f}-"
+                                                 f"{max(rd) / 1e6:.2f} | {wr:.2f} |"))
+    out += [ln for _, ln in sorted(lines, key=lambda t: -t[0])]
+    print("\n".join(out))
+    return 0
 
 
 def write_traffic(dirs, probe, command):

@@ -16,7 +16,8 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsparse_ffn.so")
+# SFN_LIBRARY names another build of the same library (the host-sanitized one)
+LIB_PATH = os.environ.get("SFN_LIBRARY") or os.path.join(_PKG, "libsparse_ffn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
