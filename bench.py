@@ -243,6 +243,17 @@ def run_calls(fn, calls):
             raise RuntimeError(f"library call failed with status {st}")
 
 
+def warm_graphs(torch, graphs):
+    """Replay every captured graph once, untimed, so that the timed pass measures steady
+    replays: a graph's first replay also uploads it to the device (several microseconds
+    per graph, which would be charged to the few calls of a short graph). The replays
+    run the same work again on the same inputs; with stacks far larger than the caches
+    no weights are left in them for the timed pass."""
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+
+
 def time_steps(torch, fn, step_args, mode):
     """Time len(step_args) steps. Graph mode captures one graph per step (each token has
     its own inputs) and replays them back to back."""
@@ -255,7 +266,7 @@ def time_steps(torch, fn, step_args, mode):
             with torch.cuda.graph(g, stream=cap):
                 run_calls(fn, [a[:-1] + (cap.cuda_stream,) for a in calls])
             graphs.append(g)
-        torch.cuda.synchronize()
+        warm_graphs(torch, graphs)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for g in graphs:
@@ -293,7 +304,7 @@ def time_mixed(torch, steps, mode):
             with torch.cuda.graph(g, stream=cap):
                 run(step, cap.cuda_stream)
             graphs.append(g)
-        torch.cuda.synchronize()
+        warm_graphs(torch, graphs)
         e0.record(stream)
         for g in graphs:
             g.replay()
