@@ -801,8 +801,14 @@ def main():
             tr = json.load(fh)
         if tr.get("kernel_hash") == kernel_hash():
             traffic = tr.get("bytes_per_call")
+    if traffic is not None and abs(args.sparsity - 0.5) > 1e-9:
+        traffic = None  # the counters were taken at k = 0.5
     roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                # the rate on the bytes the counters saw (rows plus the partials written and
+                # read back), beside the algorithmic rate above
+                "traffic_gbs": traffic / (call_us * 1e-6) / 1e9 if traffic else None,
+                "traffic_frac": traffic / (call_us * 1e-6) / 1e9 / PEAK_HBM_GBS if traffic else None,
                 "kernel": "sparse_ffn_decode call (decode_gate_local_kernel + decode_reduce_kernel), "
                           "bf16, batch 1, d 4096, f 11008",
                 "algorithmic_bytes_per_launch": per_call_bytes, "avg_launch_us": call_us, "launches": K * L,
