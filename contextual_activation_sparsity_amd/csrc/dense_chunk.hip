@@ -11,6 +11,7 @@
 // pieces of the 32 rows (Wg and Wu), one row per wave instruction, while the matrix
 // cores work on the previous stage. The four waves split each stage's K range and
 // combine through LDS at the end. H is rounded to bf16 for stage 2.
+// Layers with f > 16384 take a wide variant of stage 1 (chunk_stage1_wide_kernel below).
 // Stage 2 (down): Y = H Dt with Dt = W_down^T [f, d]. K (neurons) is the slow axis of
 // Dt: a workgroup owns 256 output columns and a range of K, loads 32 x 256 tiles (two
 // rows of 512 bytes per wave instruction), stages them in LDS and reads B fragments back
@@ -31,6 +32,10 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kKT = 512;           // stage 1: K elements per stage (1 KB of a bf16 row)
 constexpr int kLdsRow1 = kKT + 8;  // padded LDS row (elements)
+constexpr int kKTW = 256;              // wide stage 1: K elements per stage (512 bytes of a bf16 row)
+constexpr int kLdsRowW = kKTW + 8;     // its padded LDS row (elements)
+constexpr int kRowsW = 32;             // its rows per workgroup at most (two 16-neuron MFMA tiles)
+constexpr int kGW = 1024;              // its workgroups (four per compute unit, all resident)
 constexpr int kCT = 256;           // stage 2: output columns per workgroup
 constexpr int kLdsRow2 = kCT + 8;
 constexpr int kPB = 2;             // stage 2: K steps (of 32 rows) staged per batch
@@ -128,6 +133,123 @@ __global__ __launch_bounds__(256) void chunk_stage1_kernel(const char* __restric
         H[(size_t)m * hs + neuron] = 0;  // row padding read by stage 2's last K step
       }
     }
+  }
+}
+
+// Stage 1 for layers with more than 1024 16-neuron tiles (f > 16384): up to 32 neurons per
+// workgroup (two 16-neuron tiles), at most 1024 workgroups, so that all of them are
+// resident from the start (four per compute unit fit in LDS). The kernel above would run
+// f / 16 workgroups in rounds of three per compute unit: 1792 at the Llama-3-70B shape,
+// whose last round leaves two thirds of the chip idle. Each stage loads 256-element
+// (512-byte) pieces of the workgroup's rows of Wg and Wu, two rows per wave instruction;
+// otherwise it works as the kernel above. Llama-3-70B shape, 16 tokens, graph replay:
+// 233.6 against 258.9 us per layer (6.03 against 5.44 TB/s). At d 4096 (f 11008 and
+// 14336, where the kernel above runs in one round or nearly) it was slower, 76.0 against
+// 68.6 and 83.7 against 80.7 us, so those shapes keep the kernel above.
+__global__ __launch_bounds__(256) void chunk_stage1_wide_kernel(const char* __restrict__ wg, const char* __restrict__ wu,
+                                                           const float* __restrict__ bias, const char* __restrict__ x,
+                                                           int n, int d, int f, int act,
+                                                           uint16_t* __restrict__ H) {
+  // the wave sums at the end reuse this buffer
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[2][kRowsW][kLdsRowW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G1 = gridDim.x;
+  const int r0 = (int)((uint32_t)blockIdx.x * (uint32_t)f / (uint32_t)G1);
+  const int nr = (int)((uint32_t)(blockIdx.x + 1) * (uint32_t)f / (uint32_t)G1) - r0;  // <= kRowsW
+  const int col = lane & 15, q = lane >> 4;
+  const bool tok_ok = col < n;  // A side: lane's token is col
+  const int hs = (f + 7) & ~7;  // H row stride (elements)
+  const size_t rb = (size_t)d * 2;
+  const int nst = (d + kKTW - 1) / kKTW;
+  // loader: round i (0..7) of wave v reads row slot 8 i + 2 v + (lane / 32) of the 64 (the
+  // workgroup's rows of Wg, then of Wu), bytes [16 (lane % 32), +16) of the stage's
+  // 512-byte piece: two rows per wave instruction
+  uint4 wr[8], xr[2], xc[2];
+  auto load = [&](int st) {
+    const int k = st * kKTW + (lane & 31) * 8;
+    const bool kok = k < d;
+    const size_t koff = (size_t)(kok ? k : 0) * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int slot = 8 * i + 2 * wave + (lane >> 5);
+      const int rr = slot & (kRowsW - 1);
+      const bool ok = kok && rr < nr;
+      const char* base = (slot < kRowsW ? wg : wu) + (size_t)(r0 + (rr < nr ? rr : 0)) * rb;
+      const uint4 v = ldg16(base + koff);
+      wr[i] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+    // A fragments of this wave's quarter: token col, K = st kKTW + 64 wave + 32 t + 8 q
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int kx = st * kKTW + 64 * wave + 32 * t + 8 * q;
+      const bool ok = tok_ok && kx < d;
+      const uint4 v = ld16(x + (size_t)(tok_ok ? col : 0) * rb + (size_t)(kx < d ? kx : 0) * 2);
+      xr[t] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+  };
+  f32x4_t acc[2][2];  // [Wg / Wu][neurons 0-15 / 16-31]
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) acc[m][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  load(0);
+  for (int st = 0; st < nst; ++st) {
+    __syncthreads();  // the previous stage's fragments have been read
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int slot = 8 * i + 2 * wave + (lane >> 5);
+      *reinterpret_cast<uint4*>(&s_w[slot / kRowsW][slot & (kRowsW - 1)][(lane & 31) * 8]) = wr[i];
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) xc[t] = xr[t];
+    __syncthreads();
+    if (st + 1 < nst) load(st + 1);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int kk = 64 * wave + 32 * t + 8 * q;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 bg = *reinterpret_cast<const uint4*>(&s_w[0][16 * h + col][kk]);
+        const uint4 bu = *reinterpret_cast<const uint4*>(&s_w[1][16 * h + col][kk]);
+        acc[0][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_frag(xc[t]), as_frag(bg), acc[0][h], 0, 0, 0);
+        acc[1][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_frag(xc[t]), as_frag(bu), acc[1][h], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with s_w
+  f32x4_t* s_part = reinterpret_cast<f32x4_t*>(&s_w[0][0][0]);  // [wave][Wg / Wu][half][lane]
+  static_assert(4 * 2 * 2 * 64 * sizeof(f32x4_t) <= sizeof(s_w), "wave sums fit the stage buffer");
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) s_part[((wave * 2 + m) * 2 + h) * 64 + lane] = acc[m][h];
+  __syncthreads();
+  if (wave < 2) {
+    // wave h: lane holds tokens 4q + i (rows of C) for neuron r0 + 16 h + col (column of C)
+    const int h = wave;
+    f32x4_t g = s_part[((0 * 2 + 0) * 2 + h) * 64 + lane], u = s_part[((0 * 2 + 1) * 2 + h) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      g += s_part[((w * 2 + 0) * 2 + h) * 64 + lane];
+      u += s_part[((w * 2 + 1) * 2 + h) * 64 + lane];
+    }
+    const int local = 16 * h + col;
+    const int neuron = r0 + local;
+    const bool nrow_ok = local < nr;
+    const float bv = (bias && nrow_ok) ? bias[neuron] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * q + i;
+      if (m < n && nrow_ok) {
+        const float gv = g[i] + bv;
+        const float av = act == 0 ? silu_f(gv) : fmaxf(gv, 0.f);
+        H[(size_t)m * hs + neuron] = (uint16_t)f32_to_bf16_rne(av * u[i]);
+      }
+    }
+  } else if (wave == 2 && blockIdx.x == gridDim.x - 1) {
+    // row padding [f, hs) that stage 2's last K step reads
+    const int np = hs - f;
+    for (int e = lane; e < np * n; e += 64) H[(size_t)(e / np) * hs + f + e % np] = 0;
   }
 }
 
@@ -308,9 +430,18 @@ hipError_t launch_dense_chunk(const sfn_ffn& ffn, const void* x, int n, float* y
   off += (size_t)SFN_MAX_CHUNK * ((ffn.f + 7) & ~7) * sizeof(uint16_t);
   off = (off + 255) & ~(size_t)255;
   float* part = reinterpret_cast<float*>(p + off);
-  hipLaunchKernelGGL(chunk_stage1_kernel, dim3((ffn.f + 15) / 16), dim3(256), 0, stream,
-                     static_cast<const char*>(ffn.w_gate), static_cast<const char*>(ffn.w_up), ffn.b_gate,
-                     static_cast<const char*>(x), n, ffn.d, ffn.f, ffn.act, H);
+  if ((ffn.f + 15) / 16 > kGW) {
+    // enough rows that kGW workgroups of up to kRowsW rows each are all full-width
+    int g1 = kGW;
+    if (g1 < (ffn.f + kRowsW - 1) / kRowsW) g1 = (ffn.f + kRowsW - 1) / kRowsW;
+    hipLaunchKernelGGL(chunk_stage1_wide_kernel, dim3(g1), dim3(256), 0, stream,
+                       static_cast<const char*>(ffn.w_gate), static_cast<const char*>(ffn.w_up), ffn.b_gate,
+                       static_cast<const char*>(x), n, ffn.d, ffn.f, ffn.act, H);
+  } else {
+    hipLaunchKernelGGL(chunk_stage1_kernel, dim3((ffn.f + 15) / 16), dim3(256), 0, stream,
+                       static_cast<const char*>(ffn.w_gate), static_cast<const char*>(ffn.w_up), ffn.b_gate,
+                       static_cast<const char*>(x), n, ffn.d, ffn.f, ffn.act, H);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(chunk_stage2_kernel, dim3(ntile * S), dim3(256), 0, stream, H,

@@ -158,9 +158,11 @@ def test_parallel_candidate_lists(wi, d, f, act, frac):
 
 
 # ---------------------------------------------------------------------------- chunk
+# f > 16384 takes the wide stage 1 (up to 32 rows per workgroup, at most 1024 workgroups):
+# f 16400 just past the switch, 20000 with uneven shares, 40000 beyond 1024 full workgroups
 @pytest.mark.parametrize("d,f,n", [(4096, 11008, 16), (1024, 3000, 5), (512, 1001, 1), (8192, 2048, 16),
                                    (2048, 4100, 9), (8192, 28672, 16), (4096, 11008, 1), (3584, 18944, 1),
-                                   (16384, 300, 16)])
+                                   (16384, 300, 16), (256, 16400, 2), (1024, 20000, 5), (512, 40000, 3)])
 def test_dense_chunk_bf16(d, f, n):
     w = inputs.workload(4)
     say(f"[chunk] d={d} f={f} n={n}")
