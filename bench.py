@@ -321,11 +321,12 @@ def time_mixed(torch, steps, mode):
 EXTRA_LEGS = ("tiny", "b4", "b1", "70b", "chunk", "sirius", "svd")
 
 
-def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4, legs=EXTRA_LEGS, svd_layers=32,
+def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, legs=EXTRA_LEGS, svd_layers=32,
            svd_prepared=4, svd_prep_host=False):
     """The other workloads, each timed like the headline (graphs of per-layer calls, HIP
-    events over the timed steps) on n_layers independently seeded layers: per-call time,
-    algorithmic bytes and GB/s. Inputs as in the headline: on-device Gaussian weights,
+    events over the timed steps) on stacks of the workloads' own depth (32 independently
+    seeded layers at the Llama-3-8B shape, 8 at the Llama-3-70B shape, svd_layers for the
+    SVD pipelines): per-call time, algorithmic bytes and GB/s. Inputs as in the headline: on-device Gaussian weights,
     x ~ N(0, I) in bf16, thresholds from the library's own calibration. `legs` picks a
     subset (for profiling one workload at a time)."""
     import numpy as np
@@ -388,26 +389,28 @@ def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4, legs=EXTRA_
         byts = 2.0 * f * d + 4.0 * d * u + 2.0 * batch * d + 4.0 * batch * d
         out[name] = {"d": d, "f": f, "batch": batch, "sparsity": k, "layers_timed": nl, "us_per_call": us,
                      "union_density": u / f, "algorithmic_bytes_per_call": byts,
-                     "gbs": byts / (us * 1e-6) / 1e9, "tokens_per_s_32_layers": batch / (32 * us * 1e-6)}
+                     "gbs": byts / (us * 1e-6) / 1e9, "tokens_per_s_timed_stack": batch / (nl * us * 1e-6),
+                     "tokens_per_s_32_layers": batch / (32 * us * 1e-6)}
         log(f"  extra {name}: {us:.2f} us/call, union density {u / f:.4f}, {out[name]['gbs']:.0f} GB/s")
         del layers, ws, X, y
         torch.cuda.empty_cache()
 
     def chunk_leg(w4):
         # 16-token dense verification chunk at the Llama-3-70B shape
-        layers = swiglu_layers(w4, w4.d, w4.f, 2)
+        nl = w4.layers
+        layers = swiglu_layers(w4, w4.d, w4.f, nl)
         ws = B.workspace(B.sparse_ffn_workspace_size(layers[0], 16))
-        X = xtok(w4, (n_warm + n_steps, 2, 16, w4.d), inputs.STREAM_DECODE)
-        Y = torch.zeros((2, 16, w4.d), dtype=torch.float32, device=dev)
+        X = xtok(w4, (n_warm + n_steps, nl, 16, w4.d), inputs.STREAM_DECODE)
+        Y = torch.zeros((nl, 16, w4.d), dtype=torch.float32, device=dev)
         wsp, wsb = ws.data_ptr(), ws.numel()
 
         def chunk(tok, l):
             return (lib.ffn_dense_chunk, (ctypes.byref(layers[l].c), X[tok, l].data_ptr(), 16, Y[l].data_ptr(), wsp, wsb))
-        time_mixed(torch, [[chunk(tok, l) for l in range(2)] for tok in range(n_warm)], mode)
-        ms = time_mixed(torch, [[chunk(tok, l) for l in range(2)] for tok in range(n_warm, n_warm + n_steps)], mode)
-        us = ms * 1e3 / (n_steps * 2)
+        time_mixed(torch, [[chunk(tok, l) for l in range(nl)] for tok in range(n_warm)], mode)
+        ms = time_mixed(torch, [[chunk(tok, l) for l in range(nl)] for tok in range(n_warm, n_warm + n_steps)], mode)
+        us = ms * 1e3 / (n_steps * nl)
         byts = 6.0 * w4.f * w4.d + 2.0 * 16 * w4.d + 4.0 * 16 * w4.d
-        out["llama3_70b_chunk16"] = {"d": w4.d, "f": w4.f, "tokens": 16, "us_per_call": us,
+        out["llama3_70b_chunk16"] = {"d": w4.d, "f": w4.f, "tokens": 16, "layers_timed": nl, "us_per_call": us,
                                      "algorithmic_bytes_per_call": byts, "gbs": byts / (us * 1e-6) / 1e9,
                                      "tflops": 2.0 * 3 * w4.f * w4.d * 16 / (us * 1e-6) / 1e12,
                                      "ms_per_chunk_8_layers": 8 * us / 1e3}
@@ -660,15 +663,15 @@ def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4, legs=EXTRA_
     # batch of 4 with per-token masks and the union gather (Llama-3-8B shape), and batch 1
     w2 = inputs.workload(2)
     if "b4" in legs:
-        decode_leg("llama3_8b_b4_k50", w2, w2.d, w2.f, 4, 0.5, n_layers)
-        decode_leg("llama3_8b_b4_k60", w2, w2.d, w2.f, 4, 0.6, n_layers)
+        decode_leg("llama3_8b_b4_k50", w2, w2.d, w2.f, 4, 0.5, w2.layers)
+        decode_leg("llama3_8b_b4_k60", w2, w2.d, w2.f, 4, 0.6, w2.layers)
     if "b1" in legs:
-        decode_leg("llama3_8b_b1_k50", w2, w2.d, w2.f, 1, 0.5, n_layers)
-        decode_leg("llama3_8b_b1_k60", w2, w2.d, w2.f, 1, 0.6, n_layers)
+        decode_leg("llama3_8b_b1_k50", w2, w2.d, w2.f, 1, 0.5, w2.layers)
+        decode_leg("llama3_8b_b1_k60", w2, w2.d, w2.f, 1, 0.6, w2.layers)
     # sparse decode at the Llama-3-70B shape (d 8192: two 16-byte chunks per thread)
     w4 = inputs.workload(4)
     if "70b" in legs:
-        decode_leg("llama3_70b_b1_k50", w4, w4.d, w4.f, 1, 0.5, 2)
+        decode_leg("llama3_70b_b1_k50", w4, w4.d, w4.f, 1, 0.5, w4.layers)
     if "chunk" in legs:
         chunk_leg(w4)
     if "sirius" in legs:
