@@ -655,6 +655,10 @@ struct UpDownKernel {
     float wpart[kNW][VU];
     float h[64][BMAX];
     int wsum[kNW];
+    // list slots [o_lo, o_hi) around the share, loaded with the tile counts
+    int srow[kNT];
+    float sa[kNT][BMAX];
+    uint8_t sbits[kNT];
   };
 
   // Loads of one up/down step: w0 = Wu rows, w1 = Dt rows of share entries [base,
@@ -696,17 +700,28 @@ struct UpDownKernel {
       // their lists sit in the concatenation and the total n, so it can mark, for each
       // share entry inside its tiles, which list slot holds it. Then every thread copies
       // one entry.
+      // The list slots of the tiles around the share's expected place (two tiles either side
+      // of a proportional split; at most one slot per thread) are loaded together with the
+      // counts, so the gather below almost never needs a second round trip (the cumulative
+      // counts stray from the proportional split by about one tile); an entry outside the
+      // window is fetched from memory.
       int n, s0, nq;
+      const int tl = max(0, (int)((uint32_t)w * (uint32_t)a.G / (uint32_t)a.Gu) - 2);
+      const int th = min(a.G, (int)(((uint32_t)(w + 1) * (uint32_t)a.G + (uint32_t)a.Gu - 1) / (uint32_t)a.Gu) + 2);
+      const int o_lo = share_begin(tl, n_total, a.G);
+      const int o_hi = min(share_begin(th, n_total, a.G), o_lo + kNT);
       {
         const int i0 = 2 * tid;  // G <= 1024 = 2 * kNT
         const int c0 = i0 < a.G ? a.tile_cnt[i0 * kCnt] : 0;
         const int c1 = i0 + 1 < a.G ? a.tile_cnt[(i0 + 1) * kCnt] : 0;
-        int v = c0 + c1;  // inclusive scan over the wave
+        if (tid < o_hi - o_lo) {
+          const int o = o_lo + tid;
+          sm.srow[tid] = a.sel_idx[o];
+          sm.sbits[tid] = a.sel_bits[o];
 #pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-          const int u = __shfl_up(v, m, 64);
-          if (lane >= m) v += u;
+          for (int b = 0; b < BMAX; ++b) sm.sa[tid][b] = b < nb ? a.sel_a[(size_t)b * a.f + o] : 0.f;
         }
+        const int v = wave_incl_scan(c0 + c1);  // inclusive scan over the wave (DPP)
         if (lane == 63) sm.wsum[wave] = v;
         __syncthreads();
         int base = 0;
@@ -732,10 +747,18 @@ struct UpDownKernel {
       __syncthreads();
       for (int j = tid; j < nq; j += kNT) {
         const int o = sm.qslot[j];
-        sm.qrow[j] = a.sel_idx[o];
-        sm.qbits[j] = a.sel_bits[o];
+        if (o >= o_lo && o < o_hi) {
+          const int k = o - o_lo;
+          sm.qrow[j] = sm.srow[k];
+          sm.qbits[j] = sm.sbits[k];
 #pragma unroll
-        for (int b = 0; b < BMAX; ++b) sm.qa[j][b] = b < nb ? a.sel_a[(size_t)b * a.f + o] : 0.f;
+          for (int b = 0; b < BMAX; ++b) sm.qa[j][b] = sm.sa[k][b];
+        } else {
+          sm.qrow[j] = a.sel_idx[o];
+          sm.qbits[j] = a.sel_bits[o];
+#pragma unroll
+          for (int b = 0; b < BMAX; ++b) sm.qa[j][b] = b < nb ? a.sel_a[(size_t)b * a.f + o] : 0.f;
+        }
       }
       NoBalance nobal;
       stream(a, sm, nq, w, nobal);
@@ -1093,12 +1116,7 @@ struct ReduceKernel {
       c[i] = i0 + i < a.G ? a.tile_cnt[(i0 + i) * kCnt + off] : 0;
       tot += c[i];
     }
-    int v = tot;  // inclusive scan over the wave
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const int u = __shfl_up(v, m, 64);
-      if (lane >= m) v += u;
-    }
+    const int v = wave_incl_scan(tot);  // inclusive scan over the wave (DPP)
     if (lane == 63) sm.wsum[wave] = v;
     __syncthreads();
     int run = v - tot;
