@@ -30,7 +30,7 @@ def _tol(dtype):
 
 
 def _header_clear(ws):
-    """The first 2 KiB of a workspace are reserved: zero whenever no call is in flight."""
+    """The reserved header of a workspace is zero whenever no call is in flight."""
     return not bool(ws[:B.SFN_WORKSPACE_HEADER_BYTES].any().item())
 
 
@@ -394,3 +394,43 @@ def test_limits(d, f, batch):
     (f 262144: 1024 tiles of 256 rows, the most a launch takes)."""
     w = inputs.workload(1)
     _case(w, d, f, 0.5, batch, batch=batch)
+
+
+def test_concurrent_streams_with_separate_workspaces():
+    """Calls on two streams at once, each with its own workspace, give bitwise the results
+    of the same calls one after another: the library keeps no state outside the caller's
+    buffers (one-token calls at 8 KB rows, four-token batches, a calibration, and one-token
+    calls at 16 KB rows, whose tiles balance through their own workspace's header)."""
+    w = inputs.workload(1)
+    cases = [(4096, 11008, 1), (4096, 14336, 4), (8192, 6000, 1)]
+    for d, f, nb in cases:
+        say(f"[streams] d={d} f={f} B={nb}")
+        raw, dev, host = swiglu_layer_dev(w, 0, d=d, f=f)
+        layer = B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"])
+        n_tok = 6
+        xs = to_dev(inputs.tokens(w, n_tok * nb, inputs.STREAM_DECODE, d=d), "bf16").view(n_tok, nb, d)
+        xcal = to_dev(inputs.tokens(w, 64, inputs.STREAM_CAL, d=d), "bf16")
+        wss = [B.workspace(B.sparse_ffn_workspace_size(layer, 64)) for _ in range(2)]
+        t = torch.empty(2, dtype=torch.float32, device="cuda")
+        ys = torch.full((2, n_tok, nb, d), float("nan"), dtype=torch.float32, device="cuda")
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+        torch.cuda.synchronize()
+
+        def work(i, st):
+            B.sparse_ffn_calibrate(layer, xcal, 0.5 + 0.2 * i, t[i:i + 1], wss[i], stream=st)
+            for j in range(n_tok):
+                B.sparse_ffn_decode(layer, xs[j], t[i:i + 1], wss[i], y=ys[i, j], stream=st)
+
+        for i, st in enumerate(streams):  # both streams in flight together
+            with torch.cuda.stream(st):
+                work(i, st)
+        torch.cuda.synchronize()
+        together = ys.clone()
+        ys.fill_(float("nan"))
+        for i in range(2):  # the same calls one after another on the current stream
+            work(i, torch.cuda.current_stream())
+            torch.cuda.synchronize()
+        assert torch.equal(together.view(torch.int32), ys.view(torch.int32))
+        assert not torch.isnan(together).any()
+        for ws in wss:
+            assert _header_clear(ws)
