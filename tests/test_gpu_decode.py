@@ -213,6 +213,38 @@ def test_batch4_union_llama3_8b_layer(k, n_tok):
             assert normwise_err(y4[b], y1[0]) <= 1e-5
 
 
+def test_batch_shares_far_from_their_tiles():
+    """Batches whose union rows sit far from an even spread over the gate tiles (mask
+    override), so the up/down workgroups' shares of the concatenated list lie outside the
+    list slots they prefetch around their tiles and take the fallback loads: every row of
+    the first third, of the last third, each token its own quarter, a sparse comb. Per
+    token: the index list equals the mask, y against the oracle on that mask, bitwise
+    equal on a second call."""
+    w = inputs.workload(2)
+    d, f, nb = w.d, w.f, 4
+    raw, dev, host = swiglu_layer_dev(w, 0, d=d, f=f)
+    Wg, Wu, Dt = host["w_gate"], host["w_up"], host["w_down_t"]
+    layer = B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"])
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, nb))
+    xs_raw = inputs.tokens(w, nb, inputs.STREAM_DECODE, d=d)
+    xs = to_f64(xs_raw, w.dtype)
+    xd = to_dev(xs_raw, w.dtype)
+    rows = np.arange(f)
+    masks = {"first third": np.repeat((rows < f // 3)[None], nb, 0),
+             "last third": np.repeat((rows >= 2 * f // 3)[None], nb, 0),
+             "own quarter": np.stack([(rows >= b * f // 4) & (rows < (b + 1) * f // 4) for b in range(nb)]),
+             "comb": np.repeat((rows % 97 == 5)[None], nb, 0)}
+    for name, m in masks.items():
+        say(f"    {name}: union {int(m.any(0).sum())} rows")
+        y, idx, n_act = run_decode(layer, xd, None, ws, mask=m.astype(np.uint8))
+        for b in range(nb):
+            assert n_act[b] == m[b].sum() and np.array_equal(idx[b][:n_act[b]], np.flatnonzero(m[b]))
+            ref = oracle.masked_ffn(Wg, Wu, Dt, xs[b], m[b], "silu")
+            assert normwise_err(y[b], ref) <= min(TOL_BF16, fp32_output_bound(Wg, Wu, Dt, xs[b], m[b]))
+        y2, _, _ = run_decode(layer, xd, None, ws, mask=m.astype(np.uint8))
+        assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
 @pytest.mark.parametrize("batch", [2, 3])
 def test_partial_batches(batch):
     w = inputs.workload(1)
