@@ -328,7 +328,12 @@ def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, legs=EXTRA_LEGS, svd_la
     seeded layers at the Llama-3-8B shape, 8 at the Llama-3-70B shape, svd_layers for the
     SVD pipelines): per-call time, algorithmic bytes and GB/s. Inputs as in the headline: on-device Gaussian weights,
     x ~ N(0, I) in bf16, thresholds from the library's own calibration. `legs` picks a
-    subset (for profiling one workload at a time)."""
+    subset (for profiling one workload at a time).
+
+    A leg's tensors go back to torch's cache when it ends, not to the driver: for up to a
+    few seconds after several GB were released (empty_cache), the next leg's batch-4 calls
+    ran 4% slower (68.9 against 66.2 us at k 0.6); with the blocks reused, or after a
+    pause of a few seconds, they ran at the usual rate."""
     import numpy as np
     lib = B.raw()
     dev = "cuda"
@@ -393,7 +398,6 @@ def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, legs=EXTRA_LEGS, svd_la
                      "tokens_per_s_32_layers": batch / (32 * us * 1e-6)}
         log(f"  extra {name}: {us:.2f} us/call, union density {u / f:.4f}, {out[name]['gbs']:.0f} GB/s")
         del layers, ws, X, y
-        torch.cuda.empty_cache()
 
     def chunk_leg(w4):
         # 16-token dense verification chunk at the Llama-3-70B shape
@@ -416,7 +420,6 @@ def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, legs=EXTRA_LEGS, svd_la
                                      "ms_per_chunk_8_layers": 8 * us / 1e3}
         log(f"  extra chunk16: {us:.1f} us/layer, {out['llama3_70b_chunk16']['gbs']:.0f} GB/s")
         del layers, ws, X, Y
-        torch.cuda.empty_cache()
 
 
     def sirius_leg(w4):
@@ -480,7 +483,6 @@ def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, legs=EXTRA_LEGS, svd_la
             f"{dense_ms:.3f} ms, latency vs full {res['aal16']['latency_vs_full']:.3f}, divergence mean "
             f"{res['divergence']['mean']:.4f}")
         del layers, ws, X, Ys, Yd
-        torch.cuda.empty_cache()
 
 
     def svd_legs():
@@ -946,7 +948,6 @@ def table4(B, inputs, torch, mode, n_steps=16, n_warm=3, n_layers=4, shapes=T4_S
                 f"speedup {dense_us / us:.2f}")
             del cand
         del layers, ws, X, y
-        torch.cuda.empty_cache()
     return {"protocol": "fixed sparsity on every layer and projection (gate included), uniformly drawn neuron "
                         "subsets per token and layer, predictor excluded; one-pass candidate path vs dense FFN call",
             "layers_timed": n_layers, "steps": n_steps, "rows": rows}
