@@ -16,6 +16,8 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+// 4-byte alignment of an optional int32 or fp32 pointer (NULL passes)
+bool aligned4_or_null(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int wbytes(int wdtype) { return wdtype == SFN_BF16 ? 2 : 4; }
 
@@ -59,7 +61,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SFN_OK : SFN_EHIP; }
 // Validation and launch of one decode step on a workspace (sparse_ffn_decode and its
 // allocation-free variant).
 int decode_validate(const sfn_ffn* ffn, const void* x, int32_t B, const float* t, const int32_t* cand,
-                    const int32_t* n_cand, const uint8_t* mask_in, float* y) {
+                    const int32_t* n_cand, const uint8_t* mask_in, float* y, const int32_t* active_idx,
+                    const int32_t* n_active) {
   const int st = check_ffn(ffn, y != nullptr);
   if (st != SFN_OK) return st;
   if (!x) return SFN_EINVAL;
@@ -68,7 +71,9 @@ int decode_validate(const sfn_ffn* ffn, const void* x, int32_t B, const float* t
   if ((cand == nullptr) != (n_cand == nullptr)) return SFN_EINVAL;
   if (cand && (B != 1 || mask_in)) return SFN_EINVAL;
   if (y && !aligned16(y)) return SFN_EALIGN;
-  if (t && (reinterpret_cast<uintptr_t>(t) & 3u)) return SFN_EALIGN;
+  if (!aligned4_or_null(t) || !aligned4_or_null(cand) || !aligned4_or_null(n_cand) ||
+      !aligned4_or_null(active_idx) || !aligned4_or_null(n_active))
+    return SFN_EALIGN;
   return SFN_OK;
 }
 
@@ -178,7 +183,7 @@ int sparse_ffn_decode(const sfn_ffn* ffn, const void* x, int32_t B, const float*
                       const int32_t* n_cand, const uint8_t* mask_in, float* y, int32_t* active_idx,
                       int32_t* n_active, void* ws, size_t ws_bytes, void* stream) {
   try {
-    int st = decode_validate(ffn, x, B, t, cand, n_cand, mask_in, y);
+    int st = decode_validate(ffn, x, B, t, cand, n_cand, mask_in, y, active_idx, n_active);
     if (st != SFN_OK) return st;
     st = check_ws(ws, ws_bytes, decode_need(ffn, B));
     if (st != SFN_OK) return st;
@@ -192,7 +197,7 @@ int sparse_ffn_decode_noalloc(const sfn_ffn* ffn, const void* x, int32_t B, cons
                               const int32_t* n_cand, const uint8_t* mask_in, float* y, int32_t* active_idx,
                               int32_t* n_active, void* stream) {
   try {
-    int st = decode_validate(ffn, x, B, t, cand, n_cand, mask_in, y);
+    int st = decode_validate(ffn, x, B, t, cand, n_cand, mask_in, y, active_idx, n_active);
     if (st != SFN_OK) return st;
     if (decode_need(ffn, B) > kNoAllocScratchBytes) return SFN_ETOOLARGE;
     void* ws = nullptr;
@@ -211,7 +216,7 @@ int sparse_ffn_decode_parallel(const sfn_ffn* ffn, const void* x, const int32_t*
     if (st != SFN_OK) return st;
     if (!x || !cand || !n_cand || !y) return SFN_EINVAL;
     if (!aligned16(x) || !aligned16(y)) return SFN_EALIGN;
-    if (reinterpret_cast<uintptr_t>(cand) & 3u) return SFN_EALIGN;
+    if (!aligned4_or_null(cand) || !aligned4_or_null(n_cand)) return SFN_EALIGN;
     const int wb = wbytes(ffn->wdtype);
     st = check_ws(ws, ws_bytes, sfn::decode_workspace_bytes(ffn->d, ffn->f, wb, 1));
     if (st != SFN_OK) return st;

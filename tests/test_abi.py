@@ -118,6 +118,12 @@ def test_decode_validation():
     assert call(ws_bytes=2048) == B.SFN_EWORKSPACE
     assert call(ws=FAKE + 16) == B.SFN_EALIGN
     assert call(y=FAKE + 8) == B.SFN_EALIGN
+    # int32 and fp32 device pointers need 4-byte alignment
+    assert call(t=FAKE + 2) == B.SFN_EALIGN
+    assert call(cand=FAKE + 2, n_cand=FAKE) == B.SFN_EALIGN
+    assert call(cand=FAKE, n_cand=FAKE + 1) == B.SFN_EALIGN
+    assert call(idx=FAKE + 2) == B.SFN_EALIGN
+    assert call(n_act=FAKE + 3) == B.SFN_EALIGN
     assert call(ffn=ctypes.byref(_ffn(wdtype=3))) == B.SFN_EDTYPE
     assert call(ffn=ctypes.byref(_ffn(act=5))) == B.SFN_EINVAL
     assert call(ffn=ctypes.byref(_ffn(f=0))) == B.SFN_ESHAPE
@@ -148,6 +154,7 @@ def test_decode_noalloc_validation():
     assert call(cand=FAKE) == B.SFN_EINVAL
     assert call(cand=FAKE, n_cand=FAKE, B=2) == B.SFN_EINVAL
     assert call(y=FAKE + 8) == B.SFN_EALIGN
+    assert call(idx=FAKE + 2) == B.SFN_EALIGN
     assert call(ffn=ctypes.byref(_ffn(wdtype=3))) == B.SFN_EDTYPE
     # four tokens at d 8192 need 32 MiB of partials alone, more than the fixed array;
     # so does one token at f 262144 (1024 tiles of 64 KB partials at d 16384)
@@ -193,6 +200,7 @@ def test_other_calls_validation():
     assert par(y=None) == B.SFN_EINVAL
     assert par(x=FAKE + 4) == B.SFN_EALIGN
     assert par(cand=FAKE + 2) == B.SFN_EALIGN
+    assert par(n=FAKE + 2) == B.SFN_EALIGN
     assert par(ws=None) == B.SFN_EWORKSPACE
     assert par(ws_bytes=2048) == B.SFN_EWORKSPACE
     assert pred(s=B.sfn_svd(4096, 11008, 256, 0, FAKE, FAKE, None, None)) == B.SFN_EINVAL
