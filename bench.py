@@ -623,6 +623,34 @@ def extras(B, inputs, torch, mode, n_steps=16, n_warm=3, legs=EXTRA_LEGS, svd_la
             log(f"  extra {name}: {us:.2f} us/layer ({out[name]['gbs']:.0f} GB/s), "
                 f"{out[name]['speedup_over_unfused']:.2f}x the unfused calls")
 
+        # the other two pairings of predictor and pipeline (SVDP Table 2 compares the
+        # pipelines): rank 256 through the parallel pipeline, rank 1024 whitened through the
+        # sequential one, whose active count comes from an untimed pass of the fused call
+        nidx = torch.zeros((n_layers, 1), dtype=torch.int32, device=dev)
+        dap = []
+        for tok in range(n_warm, n_warm + n_steps):
+            for l in range(n_layers):
+                lib.sparse_ffn_decode_svd(ctypes.byref(layers[l].c), ctypes.byref(pred_par[l].c), X[tok, l].data_ptr(),
+                                          B.SFN_PIPE_SEQUENTIAL, y[l].data_ptr(), cand[l].data_ptr(), nidx[l].data_ptr(),
+                                          wsf.data_ptr(), wsf.numel(), torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            dap.append(nidx.float().mean().item())
+        nap = float(np.mean(dap))
+        for name, r, calls, byts in (
+                ("reglu_svd_r256_parallel_fused", 256, fused(pred_seq, B.SFN_PIPE_PARALLEL),
+                 2.0 * 256 * (d + f) + 8.0 * f + 6.0 * nc * d + 6.0 * d),
+                ("reglu_svd_r1024_whitened_sequential_fused", 1024, fused(pred_par, B.SFN_PIPE_SEQUENTIAL),
+                 2.0 * 1024 * (d + f) + 8.0 * f + 2.0 * ncp * d + 4.0 * nap * d + 6.0 * d)):
+            us = leg(calls)
+            out[name] = {"d": d, "f": f, "r": r, "s": w3.s, "layers_timed": n_layers,
+                         "distinct_layer_values": svd_prepared, "us_per_layer": us,
+                         "candidate_density": (nc if r == 256 else ncp) / f,
+                         "algorithmic_bytes_per_layer": byts, "gbs": byts / (us * 1e-6) / 1e9,
+                         "tokens_per_s": 1.0 / (n_layers * us * 1e-6)}
+            if r == 1024:
+                out[name]["active_density"] = nap / f
+            log(f"  extra {name}: {us:.2f} us/layer ({out[name]['gbs']:.0f} GB/s)")
+
     if "tiny" in legs:
         # the tiny fp32 SwiGLU layer (d 256, f 688; 2.1 MB of weights, resident in the
         # caches): latency per call, all 64 decode tokens, threshold from 256 calibration
