@@ -322,6 +322,16 @@ def pin_svd_predict_full_rank():
     assert np.allclose(oracle.svd_predict(Q1, L1, x, b), a * (c @ x) + b, atol=1e-12)
 
 
+def pin_svd_candidates_strict():
+    """A neuron is a candidate only when its prediction is strictly above its threshold
+    (SVDP Figure 3: a positive predictor value means active, and zero is not positive):
+    hand-worked predictions at, just above and just below zero and per-neuron
+    thresholds."""
+    p = np.array([0.0, 1e-12, -1e-12, 0.5, 0.75, -0.25, 2.0])
+    tau = np.array([0.0, 0.0, 0.0, 0.5, 0.5, -0.25, 2.5])
+    assert oracle.svd_candidates(p, tau).tolist() == [False, True, False, False, True, False, False]
+
+
 def pin_svd_whitened_identity():
     """Tokens whose second moment is exactly the identity (X = sqrt(n) times an
     orthonormal basis): the whitened predictor is the plain truncated SVD, L Q equal to
@@ -473,6 +483,8 @@ def pin_recall():
     assert oracle.recall(cand, act) == 3.0 / 5.0
     assert abs(oracle.false_negative_rate(cand, act) - 0.4) <= 1e-15
     assert oracle.recall(np.ones_like(act), act) == 1.0
+    # every neuron a candidate: nothing active is dropped (precision would be 5/10)
+    assert oracle.false_negative_rate(np.ones_like(act), act) == 0.0
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

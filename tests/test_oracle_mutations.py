@@ -141,6 +141,72 @@ def _band_signed_t(score, t, rel=1e-3, abs_floor=0.0):
     return np.abs(s - t) <= rel * t + abs_floor
 
 
+def _relu_leaky(g):
+    g = np.asarray(g, dtype=np.float64)
+    return np.where(g > 0.0, g, 0.01 * g)
+
+
+def _union_as_intersection(masks):
+    return np.all(np.asarray(masks, dtype=bool), axis=0)
+
+
+def _masked_ffn_inverted(Wg, Wu, Dt, x, mask, act="silu", b=None):
+    g, u = offn.gate_up(Wg, Wu, x, b)
+    h = np.where(~np.asarray(mask, dtype=bool), offn.activation(act)(g) * u, 0.0)
+    return np.asarray(Dt, dtype=np.float64).T @ h
+
+
+def _cats_decode_first_mask(Wg, Wu, Dt, X, t, act="silu", b=None, mask=None):
+    """Every token of the batch takes the first token's mask."""
+    X = np.atleast_2d(np.asarray(X, dtype=np.float64))
+    masks, scores, ys = [], [], []
+    for j in range(X.shape[0]):
+        g, _ = offn.gate_up(Wg, Wu, X[j], b)
+        a = offn.activation(act)(g)
+        if j == 0:
+            m0 = offn.cats_mask(a, t) if mask is None else np.asarray(mask[0], dtype=bool)
+        masks.append(m0)
+        scores.append(a)
+        ys.append(offn.masked_ffn(Wg, Wu, Dt, X[j], m0, act, b))
+    return np.array(masks), np.array(scores), np.array(ys)
+
+
+def _dense_chunk_no_activation(Wg, Wu, Dt, X, act="silu", b=None):
+    X = np.atleast_2d(np.asarray(X, dtype=np.float64))
+    out = []
+    for j in range(X.shape[0]):
+        g, u = offn.gate_up(Wg, Wu, X[j], b)
+        out.append(np.asarray(Dt, dtype=np.float64).T @ (g * u))
+    return np.array(out)
+
+
+def _svd_predict_bias_subtracted(Q, L, x, b=None):
+    p = np.asarray(L, dtype=np.float64) @ (np.asarray(Q, dtype=np.float64) @ np.asarray(x, dtype=np.float64))
+    return p - np.asarray(b, dtype=np.float64) if b is not None else p
+
+
+def _svd_candidates_ge(p, tau):
+    return np.asarray(p, dtype=np.float64) >= np.asarray(tau, dtype=np.float64)
+
+
+def _reglu_sequential_cand_ignored(Wg, Wu, Dt, x, cand, b=None):
+    g, u = offn.gate_up(Wg, Wu, x, b)
+    active = g > 0.0
+    h = np.where(active, offn.relu(g) * u, 0.0)
+    return active, g, np.asarray(Dt, dtype=np.float64).T @ h
+
+
+def _fnr_as_one_minus_precision(candidates, active):
+    c, a = np.asarray(candidates, dtype=bool), np.asarray(active, dtype=bool)
+    return 1.0 - float((c & a).sum()) / max(int(c.sum()), 1)
+
+
+def _period_dense_is_sparse(layers, X, thresholds, act="silu"):
+    X = np.asarray(X, dtype=np.float64)
+    ys = np.stack([offn.cats_decode(Wg, Wu, Dt, Xl, t, act=act)[2] for (Wg, Wu, Dt), Xl, t in zip(layers, X, thresholds)])
+    return ys, ys.copy()
+
+
 MUTATIONS = {
     "silu_sign": [(offn, "silu", _silu_wrong_sign)],
     "gate_bias_dropped": [(offn, "gate_up", _gate_up_no_bias), (osvd, "gate_up", _gate_up_no_bias)],
@@ -173,6 +239,26 @@ MUTATIONS = {
     "band_signed_threshold": [(offn, "within_threshold_band", _band_signed_t),
                               (oracle, "within_threshold_band", _band_signed_t)],
     "bf16_decode_shift": [(offn, "bf16_to_f64", _bf16_wrong_shift), (oracle, "bf16_to_f64", _bf16_wrong_shift)],
+    "relu_leaky": [(offn, "relu", _relu_leaky), (osvd, "relu", _relu_leaky), (oracle, "relu", _relu_leaky)],
+    "union_as_intersection": [(offn, "union_mask", _union_as_intersection),
+                              (oracle, "union_mask", _union_as_intersection)],
+    "masked_ffn_mask_inverted": [(offn, "masked_ffn", _masked_ffn_inverted), (oracle, "masked_ffn", _masked_ffn_inverted)],
+    "cats_decode_first_mask_for_all": [(offn, "cats_decode", _cats_decode_first_mask),
+                                       (osir, "cats_decode", _cats_decode_first_mask),
+                                       (oracle, "cats_decode", _cats_decode_first_mask)],
+    "dense_chunk_no_activation": [(offn, "dense_chunk", _dense_chunk_no_activation),
+                                  (osir, "dense_chunk", _dense_chunk_no_activation),
+                                  (oracle, "dense_chunk", _dense_chunk_no_activation)],
+    "svd_predict_bias_subtracted": [(osvd, "svd_predict", _svd_predict_bias_subtracted),
+                                    (oracle, "svd_predict", _svd_predict_bias_subtracted)],
+    "svd_candidates_non_strict": [(osvd, "svd_candidates", _svd_candidates_ge),
+                                  (oracle, "svd_candidates", _svd_candidates_ge)],
+    "reglu_sequential_cand_ignored": [(osvd, "reglu_sequential", _reglu_sequential_cand_ignored),
+                                      (oracle, "reglu_sequential", _reglu_sequential_cand_ignored)],
+    "fnr_as_one_minus_precision": [(odia, "false_negative_rate", _fnr_as_one_minus_precision),
+                                   (oracle, "false_negative_rate", _fnr_as_one_minus_precision)],
+    "period_dense_is_sparse": [(osir, "period_outputs", _period_dense_is_sparse),
+                               (oracle, "period_outputs", _period_dense_is_sparse)],
 }
 
 
