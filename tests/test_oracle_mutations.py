@@ -207,6 +207,40 @@ def _period_dense_is_sparse(layers, X, thresholds, act="silu"):
     return ys, ys.copy()
 
 
+def _calibrate_zero_based(Wg, Xcal, k, b=None):
+    """The K-th order statistic read with a 0-based index."""
+    X = np.atleast_2d(np.asarray(Xcal, dtype=np.float64))
+    G = X @ np.asarray(Wg, dtype=np.float64).T
+    if b is not None:
+        G = G + np.asarray(b, dtype=np.float64)[None, :]
+    S = ocal.cats_scores(G)
+    K = ocal.order_statistic_rank(k, S.size)
+    t = -1.0 if K == 0 else np.inf if K >= S.size else float(np.sort(S, axis=None)[K])
+    return t, np.float32(t), K, S
+
+
+def _gate_up_wrong_matrix(Wg, Wu, x, b=None):
+    """u taken from the gate matrix."""
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(Wg, dtype=np.float64) @ x
+    if b is not None:
+        g = g + np.asarray(b, dtype=np.float64)
+    return g, np.asarray(Wg, dtype=np.float64) @ x
+
+
+def _dense_ffn_act_on_u(Wg, Wu, Dt, x, act="silu", b=None):
+    g, u = offn.gate_up(Wg, Wu, x, b)
+    return np.asarray(Dt, dtype=np.float64).T @ (g * offn.activation(act)(u))
+
+
+def _activation_swapped(act):
+    if act == "silu":
+        return offn.relu
+    if act == "relu":
+        return offn.silu
+    raise ValueError(f"unknown activation {act!r}")
+
+
 MUTATIONS = {
     "silu_sign": [(offn, "silu", _silu_wrong_sign)],
     "gate_bias_dropped": [(offn, "gate_up", _gate_up_no_bias), (osvd, "gate_up", _gate_up_no_bias)],
@@ -257,6 +291,12 @@ MUTATIONS = {
                                       (oracle, "reglu_sequential", _reglu_sequential_cand_ignored)],
     "fnr_as_one_minus_precision": [(odia, "false_negative_rate", _fnr_as_one_minus_precision),
                                    (oracle, "false_negative_rate", _fnr_as_one_minus_precision)],
+    "calibration_zero_based_rank": [(ocal, "calibrate_cats", _calibrate_zero_based),
+                                    (oracle, "calibrate_cats", _calibrate_zero_based)],
+    "up_from_gate_matrix": [(offn, "gate_up", _gate_up_wrong_matrix), (osvd, "gate_up", _gate_up_wrong_matrix),
+                            (oracle, "gate_up", _gate_up_wrong_matrix)],
+    "activation_on_up": [(offn, "dense_ffn", _dense_ffn_act_on_u), (oracle, "dense_ffn", _dense_ffn_act_on_u)],
+    "activations_swapped": [(offn, "activation", _activation_swapped), (oracle, "activation", _activation_swapped)],
     "period_dense_is_sparse": [(osir, "period_outputs", _period_dense_is_sparse),
                                (oracle, "period_outputs", _period_dense_is_sparse)],
 }
