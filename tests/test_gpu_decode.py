@@ -346,6 +346,43 @@ def test_candidate_mode_reglu(d):
             assert np.all(y[0] == 0.0)
 
 
+@pytest.mark.parametrize("d", [2048, 8192])
+def test_candidate_entries_and_count_are_clamped(d):
+    """Candidate lists are device data the host never sees, so the kernels clamp them:
+    the count into [0, f] and every entry into [0, f). A list of every row whose first
+    entry is -3 and last is f + 7, with a count of f + 50, is therefore every row once:
+    candidate mode and the one-pass parallel call both give the dense ReGLU FFN."""
+    w = inputs.workload(3)
+    f = 3000
+    raw = inputs.reglu_layer(w, 1, d=d, f=f)
+    Wg, Wu, Dt = (to_f64(raw[k], "bf16") for k in ("w_gate", "w_up", "w_down_t"))
+    b = raw["b_gate"].astype(np.float64)
+    layer = B.FFNLayer(to_dev(raw["w_gate"], "bf16"), to_dev(raw["w_up"], "bf16"), to_dev(raw["w_down_t"], "bf16"),
+                       b_gate=torch.from_numpy(raw["b_gate"]).cuda(), act=B.SFN_ACT_RELU)
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, 1))
+    xs_raw = inputs.tokens(w, 1, inputs.STREAM_DECODE, d=d)
+    x = to_f64(xs_raw, "bf16")[0]
+    say(f"[decode] clamped candidate list d={d} f={f}")
+    lst = np.arange(f, dtype=np.int32)
+    lst[0], lst[-1] = -3, f + 7
+    cand_d = torch.from_numpy(lst).cuda()
+    n_cand = torch.tensor([f + 50], dtype=torch.int32, device="cuda")
+    every = np.ones(f, bool)
+    active, g, yo = oracle.reglu_sequential(Wg, Wu, Dt, x, every, b)
+    assert np.allclose(yo, oracle.dense_ffn(Wg, Wu, Dt, x, "relu", b))
+    sig = np.sqrt((Wg * Wg).sum(1)) * np.sqrt((x ** 2).mean())
+    y, idx, n_act = run_decode(layer, to_dev(xs_raw, "bf16"), 0.0, ws, cand=cand_d, n_cand=n_cand)
+    gm = mask_from_idx(idx[0], n_act[0], f)
+    check_mask(gm, active, g, 0.0, abs_band=1e-3 * sig)
+    _, _, y_own = oracle.reglu_sequential(Wg, Wu, Dt, x, gm, b)
+    assert normwise_err(y[0], y_own) <= TOL_BF16
+    yp = torch.full((d,), float("nan"), dtype=torch.float32, device="cuda")
+    B.sparse_ffn_decode_parallel(layer, to_dev(xs_raw[0], "bf16"), cand_d, n_cand, ws, yp)
+    torch.cuda.synchronize()
+    assert _header_clear(ws)
+    assert normwise_err(yp.cpu().numpy(), yo) <= TOL_BF16
+
+
 @pytest.mark.parametrize("d,want_y", [(1024, True), (1024, False), (8192, True)])
 def test_empty_candidate_list(d, want_y):
     """n_cand = 0 leaves every gate tile without rows (regression: a tile with no rows
