@@ -120,6 +120,16 @@ def test_wide_layers_and_f32_batches(dtype_w, d, f, batch):
     _case(w, d, f, 0.5, 2 * batch, batch=batch)
 
 
+@pytest.mark.parametrize("dtype_w,d,f,batch", [(1, 8, 1, 1), (1, 8, 17, 4), (1, 16, 3, 2), (0, 4, 5, 1),
+                                               (0, 4, 2, 3)])
+def test_degenerate_shapes(dtype_w, d, f, batch):
+    """The smallest layers: rows of one 16-byte chunk (d 8 in bf16, d 4 in fp32), a
+    single neuron, tiles with one or no rows, batches on the matrix-core gate whose tiles
+    are mostly empty."""
+    w = inputs.workload(dtype_w)
+    _case(w, d, f, 0.5, 2 * batch, batch=batch)
+
+
 @pytest.mark.parametrize("k", [0.5, 0.7])
 def test_llama2_7b_layer(k):
     w = inputs.workload(1)
