@@ -52,7 +52,7 @@ def _svd_case(d, f, r, s, n_tok, n_cal=256, rank_struct=256):
 
 
 @pytest.mark.parametrize("d,f,r", [(512, 1000, 64), (1024, 3000, 128), (2048, 700, 352), (4096, 11008, 256),
-                                   (1024, 3000, 520), (4096, 11008, 1024)])
+                                   (1024, 3000, 520), (4096, 11008, 1024), (8, 8, 8), (16, 70, 8)])
 def test_svd_predict(d, f, r):
     _svd_case(d, f, r, 0.5, 3)
 
@@ -162,7 +162,8 @@ def test_parallel_candidate_lists(wi, d, f, act, frac):
 # f 16400 just past the switch, 20000 with uneven shares, 40000 beyond 1024 full workgroups
 @pytest.mark.parametrize("d,f,n", [(4096, 11008, 16), (1024, 3000, 5), (512, 1001, 1), (8192, 2048, 16),
                                    (2048, 4100, 9), (8192, 28672, 16), (4096, 11008, 1), (3584, 18944, 1),
-                                   (16384, 300, 16), (256, 16400, 2), (1024, 20000, 5), (512, 40000, 3)])
+                                   (16384, 300, 16), (256, 16400, 2), (1024, 20000, 5), (512, 40000, 3),
+                                   (8, 1, 16), (8, 17, 5)])
 def test_dense_chunk_bf16(d, f, n):
     w = inputs.workload(4)
     say(f"[chunk] d={d} f={f} n={n}")
@@ -221,7 +222,8 @@ def test_dense_chunk_f32_and_bias_relu():
                                               (1, 4096, 11008, 256, 0.7, False), (1, 1024, 999, 33, 0.3, False),
                                               (1, 512, 700, 20, 0.0, False), (1, 512, 700, 20, 1.0, False),
                                               (1, 1024, 16500, 256, 0.5, False), (1, 512, 16384, 300, 0.5, True),
-                                              (2, 4096, 14336, 256, 0.6, False), (4, 8192, 28672, 256, 0.5, False)])
+                                              (2, 4096, 14336, 256, 0.6, False), (4, 8192, 28672, 256, 0.5, False),
+                                              (1, 8, 1, 256, 0.5, False), (0, 4, 3, 33, 0.3, True)])
 def test_calibrate(wi, d, f, n, k, bias):
     w = inputs.workload(wi)
     say(f"[calibrate] workload={wi} d={d} f={f} n={n} k={k} bias={bias}")
@@ -255,8 +257,11 @@ def test_calibrate(wi, d, f, n, k, bias):
     # ... and order statistics are 1-Lipschitz in the max norm
     assert abs(t_gpu - t64) <= err + 1e-7
     # fresh decode tokens (their own seed stream) are cut at the calibrated rate: the
-    # library's own masks under its threshold, within 0.02 of k
+    # library's own masks under its threshold, within 0.02 of k (a statistical check,
+    # made only where the 8 tokens hold thousands of neuron decisions)
     n_fresh = 8
+    if f * n_fresh < 4000:
+        return
     xs_raw = inputs.tokens(w, n_fresh, inputs.STREAM_DECODE, d=d)
     na = torch.empty(1, dtype=torch.int32, device="cuda")
     ia = torch.empty((1, f), dtype=torch.int32, device="cuda")
