@@ -513,3 +513,57 @@ def test_concurrent_streams_with_separate_workspaces():
         assert not torch.isnan(together).any()
         for ws in wss:
             assert _header_clear(ws)
+
+
+def test_host_threads_with_separate_streams():
+    """Two host threads submit calls at the same time, each on its own stream with its own
+    workspace (the binding releases the interpreter lock inside each call, so the library's
+    host code runs concurrently, including its per-device caches): bitwise the results of
+    the same calls made one after another."""
+    import threading
+    w = inputs.workload(1)
+    for d, f, nb in [(4096, 11008, 1), (8192, 6000, 1), (4096, 14336, 4)]:
+        say(f"[threads] d={d} f={f} B={nb}")
+        raw, dev, host = swiglu_layer_dev(w, 1, d=d, f=f)
+        layer = B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"])
+        n_tok = 8
+        xs = to_dev(inputs.tokens(w, n_tok * nb, inputs.STREAM_DECODE, d=d), "bf16").view(n_tok, nb, d)
+        xcal = to_dev(inputs.tokens(w, 64, inputs.STREAM_CAL, d=d), "bf16")
+        wss = [B.workspace(B.sparse_ffn_workspace_size(layer, 64)) for _ in range(2)]
+        t = torch.empty(2, dtype=torch.float32, device="cuda")
+        ys = torch.full((2, n_tok, nb, d), float("nan"), dtype=torch.float32, device="cuda")
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+        torch.cuda.synchronize()
+        start = threading.Barrier(2)
+        errors = []
+
+        def work(i, st, wait):
+            try:
+                if wait:
+                    start.wait(timeout=30)
+                with torch.cuda.stream(st):
+                    B.sparse_ffn_calibrate(layer, xcal, 0.5 + 0.2 * i, t[i:i + 1], wss[i], stream=st)
+                    for j in range(n_tok):
+                        B.sparse_ffn_decode(layer, xs[j], t[i:i + 1], wss[i], y=ys[i, j], stream=st)
+                st.synchronize()
+            except Exception as e:  # reported by the main thread
+                errors.append(e)
+
+        threads = [threading.Thread(target=work, args=(i, streams[i], True)) for i in range(2)]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join(timeout=60)
+        assert not errors, errors
+        assert not any(th.is_alive() for th in threads)
+        torch.cuda.synchronize()
+        together = ys.clone()
+        ys.fill_(float("nan"))
+        for i in range(2):  # one after another, on this thread
+            work(i, torch.cuda.current_stream(), False)
+            torch.cuda.synchronize()
+        assert not errors, errors
+        assert torch.equal(together.view(torch.int32), ys.view(torch.int32))
+        assert not torch.isnan(together).any()
+        for ws in wss:
+            assert _header_clear(ws)
