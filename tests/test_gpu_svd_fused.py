@@ -81,7 +81,8 @@ def _run(layer, pred, xd, pipeline, want_y=True):
 
 
 @pytest.mark.parametrize("d,f,r", [(4096, 11008, 256), (1024, 3000, 128), (512, 1000, 64), (256, 70000, 64),
-                                   (8192, 2048, 512), (512, 1000, 8), (4096, 11008, 1024)])
+                                   (8192, 2048, 512), (512, 1000, 8), (4096, 11008, 1024), (8, 8, 8),
+                                   (16, 70, 8)])
 def test_sequential_matches_oracle(d, f, r):
     say(f"[svd fused seq] d={d} f={f} r={r}")
     w, (Wg, Wu, Dt, b, Q64, L64, tau), layer, pred = _setup(d, f, r)
@@ -101,7 +102,8 @@ def test_sequential_matches_oracle(d, f, r):
 
 
 @pytest.mark.parametrize("d,f,r,act", [(4096, 11008, 1024, "relu"), (4096, 11008, 256, "silu"),
-                                       (1024, 3000, 128, "relu"), (256, 70000, 64, "silu"), (512, 1000, 8, "relu")])
+                                       (1024, 3000, 128, "relu"), (256, 70000, 64, "silu"), (512, 1000, 8, "relu"),
+                                       (8, 8, 8, "relu"), (16, 70, 8, "silu")])
 def test_parallel_matches_oracle(d, f, r, act):
     say(f"[svd fused par] d={d} f={f} r={r} act={act}")
     w, (Wg, Wu, Dt, b, Q64, L64, tau), layer, pred = _setup(d, f, r, act=act)
