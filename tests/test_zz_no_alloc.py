@@ -59,3 +59,48 @@ def test_noalloc_matches_workspace_decode():
         a, b = _both(layer, xs, 0.265, nb)
         _check(a, b, f"call {i}")
         say(f"    active {a[2].tolist()} of {f}: identical")
+
+
+def test_noalloc_in_a_graph():
+    """Graph capture, the use the allocation-free call exists for: one call at 8 KB rows
+    and one at d 8192 (whose tiles balance through the scratch array's header) captured in
+    one graph, replayed three times with workspace calls in between; every replay gives
+    the eager results bit for bit. An eager call comes first, so the array's address is
+    already resolved when capture starts."""
+    w = inputs.workload(1)
+    cases = [(4096, 11008), (8192, 6000)]
+    layers, xs, ys, want = [], [], [], []
+    t = torch.tensor([0.265], dtype=torch.float32, device="cuda")
+    for d, f in cases:
+        raw, dev, _ = swiglu_layer_dev(w, 2, d=d, f=f)
+        layer = B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"])
+        x = to_dev(inputs.tokens(w, 1, inputs.STREAM_DECODE, d=d), "bf16")
+        y = torch.full((1, d), float("nan"), dtype=torch.float32, device="cuda")
+        B.sparse_ffn_decode_noalloc(layer, x, t, y=y)
+        torch.cuda.synchronize()
+        layers.append(layer)
+        xs.append(x)
+        ys.append(y)
+        want.append(y.clone())
+    other = B.FFNLayer(*swiglu_layer_dev(w, 3, d=1024, f=2000)[1].values())
+    ws = B.workspace(B.sparse_ffn_workspace_size(other, 4))
+    x4 = to_dev(inputs.tokens(w, 4, inputs.STREAM_CAL, d=1024), "bf16")
+    y4 = torch.empty((4, 1024), dtype=torch.float32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    for y in ys:
+        y.fill_(float("nan"))
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        for layer, x, y in zip(layers, xs, ys):
+            B.sparse_ffn_decode_noalloc(layer, x, t, y=y, stream=cap)
+    for rep in range(3):
+        say(f"[noalloc graph] replay {rep}")
+        for y in ys:
+            y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for (d, f), y, yw in zip(cases, ys, want):
+            assert torch.equal(y.view(torch.int32), yw.view(torch.int32)), (rep, d, f)
+        B.sparse_ffn_decode(other, x4, t, ws, y=y4)  # eager work between the replays
+        torch.cuda.synchronize()
