@@ -139,6 +139,12 @@ __device__ __forceinline__ void st_through(SFN_GLOBAL uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint32_t ld_through(const SFN_GLOBAL uint32_t* p) {
   return __hip_atomic_load((uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Sets *p to v if it holds expect; returns the value found (== expect iff it was set).
+__device__ __forceinline__ uint32_t cas_through(SFN_GLOBAL uint32_t* p, uint32_t expect, uint32_t v) {
+  __hip_atomic_compare_exchange_strong((uint32_t*)p, &expect, v, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return expect;
+}
 
 template <int WT, int BMAX, int CPT, int TPR, int R>
 struct Shape {
@@ -1135,9 +1141,11 @@ struct ReduceKernel {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ri = blockIdx.x;
     const int nb = a.nb;
-    // the balancer's count words go back to zero for the next call
-    if (a.flags)
+    // the balancer's count words and its decision go back to zero for the next call
+    if (a.flags) {
       for (int i = ri * kRT + tid; i < a.G; i += gridDim.x * kRT) a.flags[i] = 0u;
+      if (ri == 0 && tid == 0) a.flags[kWsBalDecisionWord] = 0u;
+    }
     if (a.y && ri < a.n_red) {
       const int L = nb * a.d;
       const int nck = (L + kRedCols - 1) / kRedCols;
@@ -1208,6 +1216,15 @@ __global__ __launch_bounds__(kNT) void decode_gate_kernel(DecodeArgs a) {
 // on the counts only, so every workgroup sums the same rows in the same order on every
 // run and y stays deterministic. The counts live in the workspace header, which the
 // reduce kernel clears again.
+// Waiting for every count is safe only if every tile is resident, which a launch does not
+// guarantee: with two such calls in flight on different streams, each can hold part of
+// the device while its other tiles wait for it. So the launch first settles, in one header
+// word, whether it balances at all. The last workgroup, on starting, swaps the word from 0
+// to "yes": workgroups are dispatched in index order, so all the others have started, and
+// none can finish before the decision, so all are resident. Workgroup 0 (always resident)
+// swaps it from 0 to "no" if it is still unset a few microseconds after its own decision
+// point. The first swap wins and every workgroup follows the word: "no" means each tile
+// keeps its own rows and waits for nothing else.
 // It costs a write-through of the tile's list and a wait for it, the count round trip,
 // and for a workgroup that takes rows, a round trip for their entries. That pays only
 // where tiles carry much up/down work: rows wider than 8 KB. One token, graph replay:
@@ -1219,6 +1236,7 @@ constexpr int kBalMaxTiles = 256;
 constexpr uint32_t kPublished = 0x80000000u;
 
 struct BalSmem {
+  uint32_t decision;  // the launch's kBalYes / kBalNo, or 0 if it never arrived
   int cnt[kBalMaxTiles];
   int epre[kBalMaxTiles + 1];  // entries given away by the tiles before t
   int dpre[kBalMaxTiles + 1];  // shortfalls of the tiles before t
@@ -1231,6 +1249,7 @@ struct Balancer {
   bool on;
   int G, w, nown, n_total;
   uint32_t cw;           // count word of tile threadIdx.x, loaded when the up/down starts
+  uint32_t dw0 = 0;      // thread 0: the decision word, loaded with the counts
   bool gave_up = false;  // a count never arrived: this workgroup's partial becomes NaN
 
   __device__ bool active() const { return on; }
@@ -1243,15 +1262,43 @@ struct Balancer {
   // the time they are used, one step later)
   __device__ void load_counts(const DevArgs& a) {
     if ((int)threadIdx.x < G) cw = ld_through(a.flags + threadIdx.x);
+    if (threadIdx.x == 0) dw0 = ld_through(a.flags + kWsBalDecisionWord);
   }
 
   // Every tile's count (waiting for tiles still gating), the assignment, and this
   // workgroup's list: its first keep entries, then its share of the given-away ones
   // appended. Returns the list length.
+  // polls of workgroup 0 for the last workgroup's "yes" before it decides "no"
+  static constexpr uint32_t kDecideSpins = 4;
+
   template <class SmemT>
   __device__ int decide(const DevArgs& a, SmemT& sm, int covered) {
     (void)covered;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the launch's decision (see above); the wait for it ends because workgroup 0 is
+    // resident, and is bounded all the same
+    if (tid == 0) {
+      SFN_GLOBAL uint32_t* dw = a.flags + kWsBalDecisionWord;
+      uint32_t dv = dw0;
+      const uint32_t bound = w == 0 ? kDecideSpins : (1u << 20);
+      for (uint32_t spins = 0; dv == 0u && spins < bound; ++spins) {
+        __builtin_amdgcn_s_sleep(2);
+        dv = ld_through(dw);
+      }
+      if (dv == 0u && w == 0) {
+        const uint32_t found = cas_through(dw, 0u, kBalNo);
+        dv = found == 0u ? kBalNo : found;
+      }
+      bs.decision = dv;
+    }
+    __syncthreads();
+    if (bs.decision != kBalYes) {
+      if (bs.decision != kBalNo) {  // never decided: poison, as for a count that never came
+        gave_up = true;
+        if (tid == 0) st_through(a.flags + kWsStatusWord, kStatusBalancer);
+      }
+      return nown;  // every tile streams all of its own entries
+    }
     // Every tile is resident at once (G <= CU count), so the wait ends once all have been
     // dispatched; kernels of other streams can only delay that. The bound (2^20 round
     // trips, about a second) is a guard: a workgroup that reaches it poisons its partial,
@@ -1339,6 +1386,10 @@ __global__ __launch_bounds__(kNT) void decode_gate_local_kernel(DecodeArgs args)
   static_assert(BMAX == 1, "one token");
   __shared__ typename UD::Smem usm;
   __shared__ BalSmem bsm;
+  // balanced launch: the last workgroup to be dispatched settles "yes" if nothing has
+  // settled the launch yet (the decision word in the header; see Balancer)
+  if (args.flags && blockIdx.x == gridDim.x - 1 && threadIdx.x == 0)
+    (void)cas_through(gp(args.flags) + kWsBalDecisionWord, 0u, kBalYes);
   const int2 go = GateKernel<WT, BMAX, CPT, TPR, RGATE>::template run<true>(
       args, [&](int slot, int row, const auto& av, uint32_t bits) {
         usm.qrow[slot] = row;

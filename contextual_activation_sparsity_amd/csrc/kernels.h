@@ -16,12 +16,17 @@ namespace sfn {
 //     words [0, 256)      the one-token decode's tile counts (balancer)
 //     word kWsStatusWord  status: 0, or the code of a bounded device wait that gave up
 //                         (left set for the caller to read; see sparse_ffn.h)
+//     word kWsBalDecisionWord  the balancer's decision for the call in flight: 0 until
+//                         decided, then kBalYes or kBalNo (cleared by the reduce kernel)
 //   [kWsHeader, ...)    per-call scratch, rewritten by each call before it is read
 // Scratch of one call may overlap scratch of another.
 constexpr size_t kWsHeader = SFN_WORKSPACE_HEADER_BYTES;
 constexpr int kWsStatusWord = SFN_WORKSPACE_STATUS_OFFSET / 4;
 constexpr uint32_t kStatusBalancer = SFN_STATUS_BALANCER_TIMEOUT;
 constexpr uint32_t kStatusPredictor = SFN_STATUS_PREDICTOR_TIMEOUT;
+constexpr int kWsBalDecisionWord = kWsStatusWord + 1;
+constexpr uint32_t kBalYes = 1u;  // every tile of the launch is resident: balance
+constexpr uint32_t kBalNo = 2u;   // some tile was not dispatched in time: each keeps its own rows
 
 struct DecodeArgs {
   const char* wg;

@@ -51,7 +51,9 @@
  *     *n_cand is -1). The word stays set for the caller to read after a
  *     synchronisation; zero the whole header again before the workspace is reused.
  *   - Outputs are deterministic: identical inputs give bitwise identical y, index
- *     lists and thresholds (fixed reduction orders, no floating-point atomics).
+ *     lists and thresholds (fixed reduction orders, no floating-point atomics). One
+ *     exception, for calls that overlap on the device: see sparse_ffn_decode (one token,
+ *     rows wider than 8 KB).
  *   - Arithmetic: products and sums in fp32 (bf16 inputs are widened exactly).
  */
 #ifndef SPARSE_FFN_H
@@ -165,11 +167,14 @@ int sparse_ffn_calibrate(const sfn_ffn* ffn, const void* x_cal, int32_t n, float
  * active_idx [B, f] int32 / n_active [B] int32 (device) or NULL: token b's active
  *   neurons in ascending order and their count.
  * One token with rows wider than 8 KB (d > 4096 in bf16): the workgroups of the call
- *   share out their up/down rows, so each waits until all of them have run their gate
- *   part. On a device with at least as many compute units as workgroups they are all
- *   resident at once; kernels on other streams can only delay them. Should the wait
- *   exceed about a second, y comes out NaN rather than wrong and the workspace status
- *   word reads SFN_STATUS_BALANCER_TIMEOUT.
+ *   share out their up/down rows, each waiting until all of them have run their gate
+ *   part, but only when all of them are resident at once, which the call finds out for
+ *   itself. When they are not (another such call in flight on another stream, or other
+ *   work holding compute units), each workgroup keeps its own rows and waits for nothing.
+ *   The two ways add the rows in different orders: y is bitwise repeatable for calls that
+ *   do not overlap, and otherwise equal to fp32 rounding. Should a wait still exceed about
+ *   a second, y comes out NaN rather than wrong and the workspace status word reads
+ *   SFN_STATUS_BALANCER_TIMEOUT.
  */
 int sparse_ffn_decode(const sfn_ffn* ffn, const void* x, int32_t B, const float* t,
                       const int32_t* cand, const int32_t* n_cand, const uint8_t* mask_in,

@@ -475,11 +475,25 @@ def test_limits(d, f, batch):
     _case(w, d, f, 0.5, batch, batch=batch)
 
 
+def _same_as_sequential(together, seq, d):
+    """Overlapping calls give the sequential results bit for bit, except one-token calls
+    on rows wider than 8 KB (d > 4096 in bf16): a call whose tiles are not all resident at
+    once keeps its rows unbalanced and sums them in another order, so there the results
+    agree to fp32 rounding."""
+    assert not torch.isnan(together).any()
+    if d <= 4096:
+        assert torch.equal(together.view(torch.int32), seq.view(torch.int32))
+    else:
+        err = (together - seq).abs().amax(dim=-1) / seq.abs().amax(dim=-1)
+        assert float(err.max()) <= 1e-5, float(err.max())
+
+
 def test_concurrent_streams_with_separate_workspaces():
-    """Calls on two streams at once, each with its own workspace, give bitwise the results
-    of the same calls one after another: the library keeps no state outside the caller's
-    buffers (one-token calls at 8 KB rows, four-token batches, a calibration, and one-token
-    calls at 16 KB rows, whose tiles balance through their own workspace's header)."""
+    """Calls on two streams at once, each with its own workspace, give the results of the
+    same calls one after another: the library keeps no state outside the caller's buffers
+    (one-token calls at 8 KB rows, four-token batches, a calibration, and one-token calls
+    at 16 KB rows, whose tiles balance through their own workspace's header when all of
+    them are resident)."""
     w = inputs.workload(1)
     cases = [(4096, 11008, 1), (4096, 14336, 4), (8192, 6000, 1)]
     for d, f, nb in cases:
@@ -509,8 +523,7 @@ def test_concurrent_streams_with_separate_workspaces():
         for i in range(2):  # the same calls one after another on the current stream
             work(i, torch.cuda.current_stream())
             torch.cuda.synchronize()
-        assert torch.equal(together.view(torch.int32), ys.view(torch.int32))
-        assert not torch.isnan(together).any()
+        _same_as_sequential(together, ys, d)
         for ws in wss:
             assert _header_clear(ws)
 
@@ -518,8 +531,11 @@ def test_concurrent_streams_with_separate_workspaces():
 def test_host_threads_with_separate_streams():
     """Two host threads submit calls at the same time, each on its own stream with its own
     workspace (the binding releases the interpreter lock inside each call, so the library's
-    host code runs concurrently, including its per-device caches): bitwise the results of
-    the same calls made one after another."""
+    host code runs concurrently, including its per-device caches): the results of the same
+    calls made one after another. At d 8192 two balanced one-token calls can overlap on the
+    device; a call whose tiles are not all resident, because the other call holds compute
+    units, does not wait for them but keeps its rows unbalanced (results equal to fp32
+    rounding, never NaN)."""
     import threading
     w = inputs.workload(1)
     for d, f, nb in [(4096, 11008, 1), (8192, 6000, 1), (4096, 14336, 4)]:
@@ -563,7 +579,6 @@ def test_host_threads_with_separate_streams():
             work(i, torch.cuda.current_stream(), False)
             torch.cuda.synchronize()
         assert not errors, errors
-        assert torch.equal(together.view(torch.int32), ys.view(torch.int32))
-        assert not torch.isnan(together).any()
+        _same_as_sequential(together, ys, d)
         for ws in wss:
             assert _header_clear(ws)
