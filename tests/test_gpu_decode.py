@@ -196,6 +196,38 @@ def test_balanced_tiles_uneven_counts():
         assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
 
 
+def test_balancing_declined_keeps_each_tiles_rows():
+    """The path a launch takes when not all of its tiles are resident (another such call
+    in flight): forced here from the host by writing "no" into the decision word of the
+    workspace header before the call, so the last workgroup's "yes" finds it taken. Every
+    tile then streams its own rows: y against the oracle on the library's mask within the
+    fp32 bound, the same mask as the balanced call, header zero and no status afterwards."""
+    w = inputs.workload(4)
+    d, f, k = 8192, 6000, 0.5
+    raw, dev, host = swiglu_layer_dev(w, 0, d=d, f=f)
+    Wg, Wu, Dt = host["w_gate"], host["w_up"], host["w_down_t"]
+    layer = B.FFNLayer(dev["w_gate"], dev["w_up"], dev["w_down_t"])
+    ws = B.workspace(B.sparse_ffn_workspace_size(layer, 1))
+    xcal = to_f64(inputs.tokens(w, w.n_cal, inputs.STREAM_CAL, d=d), w.dtype)
+    t = float(oracle.calibrate_cats(Wg, xcal, k)[1])
+    x_raw = inputs.tokens(w, 2, inputs.STREAM_DECODE, d=d)
+    decision = B.SFN_WORKSPACE_STATUS_OFFSET + 4  # the word after the status word
+    for j in range(2):
+        xd = to_dev(x_raw[j:j + 1], w.dtype)
+        yb, ib, nb_ = run_decode(layer, xd, t, ws)  # balanced (nothing overlaps)
+        ws[decision:decision + 4] = torch.tensor([2, 0, 0, 0], dtype=torch.uint8, device="cuda")
+        y, idx, n_act = run_decode(layer, xd, t, ws)  # checks the header is zero again
+        assert B.workspace_status(ws) == 0
+        gm = mask_from_idx(idx[0], n_act[0], f)
+        assert n_act[0] == nb_[0] and np.array_equal(idx[0][:n_act[0]], ib[0][:nb_[0]])
+        x = to_f64(x_raw, w.dtype)[j]
+        e = normwise_err(y[0], oracle.masked_ffn(Wg, Wu, Dt, x, gm, "silu"))
+        assert e <= min(TOL_BF16, fp32_output_bound(Wg, Wu, Dt, x, gm, "silu")), e
+        say(f"    token {j}: {n_act[0]} active, error {e:.2e}, "
+            f"{'bitwise equal to' if np.array_equal(y.view(np.uint32), yb.view(np.uint32)) else 'differs from'} "
+            f"the balanced call")
+
+
 def test_qwen2_7b_layer():
     """SparseQwen2-7B FFN shape: d 3584 is 448 16-byte chunks, not a power of two, so
     part of each row's threads hold no chunk."""
