@@ -1094,18 +1094,23 @@ struct ParKernel {
 
 // ---------------------------------------------------------------------- reduce kernel
 // y = sum of the partials of the up/down kernel, in chunks of 32 columns (128 bytes of
-// each partial row): lane l of group g sums column l of partials g, g + 16, g + 32, ...
-// (16 loads in flight), then group 0 adds the 16 group sums in order, so y is
-// deterministic. The partials are read once, with non-temporal loads (0.2-0.3 us per
-// one-token call and 1.7 us per four-token call faster than plain loads at d 4096). The
-// workgroups also assemble the per-token active index lists.
+// each partial row). Thread (g, q) of 64 groups x 8 column quads sums 16-byte quad q of
+// partials g, g + 64, g + 128, ... (four loads in flight per round, rounds past the last
+// partial row masked, so a short list of partials costs one round trip, not one per
+// row); then eight threads per column add eight groups each, in order, and one thread
+// per column adds those eight, so y is deterministic. The partials are read once, with
+// non-temporal loads (0.2-0.3 us per one-token call and 1.7 us per four-token call faster
+// than plain loads at d 4096). The workgroups also assemble the per-token active index
+// lists.
 constexpr int kRedCols = 32;
-constexpr int kRedGroups = 16;
 
 struct ReduceKernel {
-  static constexpr int kRT = kRedCols * kRedGroups;  // 512 threads
+  static constexpr int kRT = 512;                // threads
+  static constexpr int kQC = kRedCols / 4;       // 16-byte column quads per chunk
+  static constexpr int kNG = kRT / kQC;          // partial-row groups (64)
   struct Smem {
-    float red[kRedGroups][kRedCols];
+    float red4[kNG][kRedCols];   // group sums
+    float red8[8][kRedCols];     // sums of eight groups
     int pref[kGMax + 1];
     int wsum[kRT / 64];
   };
@@ -1147,31 +1152,43 @@ struct ReduceKernel {
       if (ri == 0 && tid == 0) a.flags[kWsBalDecisionWord] = 0u;
     }
     if (a.y && ri < a.n_red) {
-      const int L = nb * a.d;
+      const int L = nb * a.d;  // a multiple of 4: rows are whole 16-byte chunks
       const int nck = (L + kRedCols - 1) / kRedCols;
       const int c0 = share_begin(ri, nck, a.n_red), c1 = share_begin(ri + 1, nck, a.n_red);
-      const int col = tid % kRedCols, g = tid / kRedCols;
+      const int qd = tid % kQC, g = tid / kQC;
       for (int ck = c0; ck < c1; ++ck) {
-        const int e = ck * kRedCols + col;
+        const int e = ck * kRedCols + 4 * qd;
         const bool ok = e < L;
         const SFN_GLOBAL float* src = a.part + (ok ? e : 0);
-        float sum = 0.f;
-        int p = g;
-        for (; p + (kRedGroups - 1) * kRedGroups < P; p += kRedGroups * kRedGroups) {
-          float v[kRedGroups];
+        f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+        for (int p = g; p < P; p += 4 * kNG) {
+          f32x4_t v[4];
 #pragma unroll
-          for (int u = 0; u < kRedGroups; ++u) v[u] = __builtin_nontemporal_load(src + (size_t)(p + u * kRedGroups) * L);
+          for (int u = 0; u < 4; ++u) {
+            const int pu = p + u * kNG;
+            v[u] = pu < P ? __builtin_nontemporal_load(reinterpret_cast<const SFN_GLOBAL f32x4_t*>(src + (size_t)pu * L))
+                          : f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
 #pragma unroll
-          for (int u = 0; u < kRedGroups; ++u) sum += v[u];
+          for (int u = 0; u < 4; ++u) sum += v[u];
         }
-        for (; p < P; p += kRedGroups) sum += __builtin_nontemporal_load(src + (size_t)p * L);
-        sm.red[g][col] = sum;
-        __syncthreads();
-        if (g == 0 && ok) {
-          float tot = sm.red[0][col];
 #pragma unroll
-          for (int j = 1; j < kRedGroups; ++j) tot += sm.red[j][col];
-          a.y[e] = tot;
+        for (int j = 0; j < 4; ++j) sm.red4[g][4 * qd + j] = sum[j];
+        __syncthreads();
+        if (tid < 8 * kRedCols) {
+          const int col = tid % kRedCols, h = tid / kRedCols;
+          float t8 = sm.red4[8 * h][col];
+#pragma unroll
+          for (int j = 1; j < 8; ++j) t8 += sm.red4[8 * h + j][col];
+          sm.red8[h][col] = t8;
+        }
+        __syncthreads();
+        if (tid < kRedCols) {
+          const int ee = ck * kRedCols + tid;
+          float tot = sm.red8[0][tid];
+#pragma unroll
+          for (int j = 1; j < 8; ++j) tot += sm.red8[j][tid];
+          if (ee < L) a.y[ee] = tot;
         }
         __syncthreads();
       }
