@@ -1099,15 +1099,15 @@ struct ParKernel {
 // partial row masked, so a short list of partials costs one round trip, not one per
 // row); then eight threads per column add eight groups each, in order, and one thread
 // per column adds those eight, so y is deterministic. The partials are read once, with
-// non-temporal loads (0.2-0.3 us per one-token call and 1.7 us per four-token call faster
-// than plain loads at d 4096). The workgroups also assemble the per-token active index
-// lists.
+// non-temporal loads (with the earlier 4-byte loads these were 0.2-0.3 us per one-token
+// call and 1.7 us per four-token call faster than plain loads at d 4096). The workgroups
+// also assemble the per-token active index lists.
 constexpr int kRedCols = 32;
 
 struct ReduceKernel {
   static constexpr int kRT = 512;                // threads
   static constexpr int kQC = kRedCols / 4;       // 16-byte column quads per chunk
-  static constexpr int kNG = kRT / kQC;          // partial-row groups (64)
+  static constexpr int kNG = kRT / kQC;          // partial-row groups (64 = 8 x 8 in the sums below)
   struct Smem {
     float red4[kNG][kRedCols];   // group sums
     float red8[8][kRedCols];     // sums of eight groups
