@@ -120,6 +120,23 @@ def test_wide_layers_and_f32_batches(dtype_w, d, f, batch):
     _case(w, d, f, 0.5, 2 * batch, batch=batch)
 
 
+@pytest.mark.parametrize("d,f,batch", [(40, 504, 1), (512, 512, 1), (512, 520, 1), (128, 2040, 1), (64, 65800, 1),
+                                       (40, 520, 3)])
+def test_partial_row_counts_around_reduce_rounds(d, f, batch):
+    """Partial-row counts on either side of the reduce kernel's rounds of 64 and 256 rows
+    (63, 64, 65, 255 and 258 workgroups, one partial row each), and rows whose 32-column
+    chunks end part-way (d 40): against the oracle within the fp32 bound, which a dropped
+    or doubled partial row exceeds, and bitwise the same over repeated calls."""
+    w = inputs.workload(1)
+    layer, ws, _, _, t = _case(w, d, f, 0.5, 2 * batch, batch=batch)
+    xd = to_dev(inputs.tokens(w, batch, inputs.STREAM_DECODE, d=d), w.dtype)
+    y_a, idx_a, n_a = run_decode(layer, xd, t, ws)
+    for _ in range(2):
+        y_b, idx_b, n_b = run_decode(layer, xd, t, ws)
+        assert np.array_equal(y_a.view(np.uint32), y_b.view(np.uint32))
+        assert np.array_equal(idx_a, idx_b) and np.array_equal(n_a, n_b)
+
+
 @pytest.mark.parametrize("dtype_w,d,f,batch", [(1, 8, 1, 1), (1, 8, 17, 4), (1, 16, 3, 2), (0, 4, 5, 1),
                                                (0, 4, 2, 3)])
 def test_degenerate_shapes(dtype_w, d, f, batch):
