@@ -196,7 +196,8 @@ int sparse_ffn_decode(const sfn_ffn* ffn, const void* x, int32_t B, const float*
  * sparse_ffn_decode leaves a workspace, so calls in order on one stream (or with a
  * synchronisation between them) are safe. Calls that can overlap on one GPU (different
  * streams, or several host threads) race on the array and give wrong results. A bounded
- * wait that gives up shows as NaN in y (the array's status word is not exposed).
+ * wait that gives up shows as NaN in y. The array's status word is not exposed; a give-up
+ * leaves it set, and no later call reads it.
  */
 int sparse_ffn_decode_noalloc(const sfn_ffn* ffn, const void* x, int32_t B, const float* t,
                               const int32_t* cand, const int32_t* n_cand, const uint8_t* mask_in,
