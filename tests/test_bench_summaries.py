@@ -98,3 +98,13 @@ def test_kernel_trace_groups_by_instance_and_grid(tmp_path, capsys):
     assert "| `decode_reduce_kernel` | 128 x 512 | 1 | 4.00 |" in out
     assert "| `decode_reduce_kernel` | 512 x 512 | 1 | 8.00 |" in out
     assert "| (torch kernels: input generation, copies) | | 1 | 1.00 |" in out
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU: --gpus above 1 exits with status 2 and says so,
+    before anything touches a device."""
+    import subprocess
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU only" in res.stderr and res.stdout == ""
